@@ -1,0 +1,280 @@
+// gqa_attn_abi.cpp - the C ABI of libgqa_attn.so: argument checks, split planning,
+// workspace management and launches on the caller's stream. The declarations and the
+// contract of every entry point are in include/gqa_attn.h.
+#include "gqa_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "gqa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int hip_fail(const char* what, int err) {
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), "%s: %s (%d)", what, hipGetErrorString((hipError_t)err), err);
+  g_last_error = buf;
+  return GQA_ATTN_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr double kLog2e = 1.4426950408889634;
+constexpr long long kMaxGridY = 65535;
+
+// Shared shape checks. Returns 0 or an error code.
+int check_heads(int Hq, int Hkv, int D, float scale) {
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return GQA_ATTN_ERR_DIM;
+  if (!std::isfinite(scale)) return GQA_ATTN_ERR_DIM;
+  if (D != 128) return GQA_ATTN_ERR_UNSUPPORTED;
+  return 0;
+}
+
+// Elements of a [n0, n1, n2, 128] tensor, or -1 if that overflows 2^62.
+long long elems4(long long n0, long long n1, long long n2) {
+  const long long lim = (1LL << 62) / 128;
+  if (n0 > lim / n1) return -1;
+  long long x = n0 * n1;
+  if (x > lim / n2) return -1;
+  return x * n2 * 128;
+}
+
+struct DecodeShapeCheck {
+  int code;
+  int chunk;
+  int nsplit;
+  int hgroups;
+};
+
+DecodeShapeCheck check_decode_shape(int B, int L, int Hq, int Hkv, int D, float scale, int chunk) {
+  DecodeShapeCheck r{0, 0, 0, 0};
+  if (B < 1 || L < 1) { r.code = GQA_ATTN_ERR_DIM; return r; }
+  if ((r.code = check_heads(Hq, Hkv, D, scale)) != 0) return r;
+  if (elems4(B, L, Hkv) < 0 || elems4(B, Hq, 1) < 0) { r.code = GQA_ATTN_ERR_DIM; return r; }
+  const int G = Hq / Hkv;
+  r.hgroups = (G + 15) / 16;
+  if (B > kMaxGridY || (long long)Hkv * r.hgroups > kMaxGridY) { r.code = GQA_ATTN_ERR_DIM; return r; }
+  if (chunk == 0) chunk = gqa::decode_default_chunk(B, L, Hkv, G);
+  if (chunk < 64 || chunk % 64 != 0 || chunk > gqa::kMaxChunk) { r.code = GQA_ATTN_ERR_WORKSPACE; return r; }
+  r.chunk = chunk;
+  r.nsplit = (int)(((long long)L + chunk - 1) / chunk);
+  if (elems4(B, Hq, r.nsplit) < 0) { r.code = GQA_ATTN_ERR_DIM; return r; }
+  return r;
+}
+
+size_t ws_bytes_for(int B, int Hq, int nsplit) {
+  const size_t rows = (size_t)B * Hq * nsplit;
+  const size_t obytes = (rows * 128 * sizeof(float) + 255) / 256 * 256;
+  return obytes + (rows * sizeof(float) + 255) / 256 * 256;
+}
+
+// Library-owned decode workspaces, one per (device, stream), grown on demand.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, void*>, Workspace> g_ws;
+
+int get_workspace(size_t need, hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace& w = g_ws[{dev, (void*)stream}];
+  if (w.bytes < need) {
+    if (w.ptr) {
+      // Earlier decodes on this stream may still read the old buffer.
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail("hipStreamSynchronize", e);
+      e = hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+      if (e != hipSuccess) return hip_fail("hipFree", e);
+    }
+    const size_t grow = (need + (1u << 20) - 1) / (1u << 20) * (1u << 20);
+    e = hipMalloc(&w.ptr, grow);
+    if (e != hipSuccess) { w.ptr = nullptr; return hip_fail("hipMalloc(decode workspace)", e); }
+    w.bytes = grow;
+  }
+  *out = w.ptr;
+  return 0;
+}
+
+gqa::DecodeArgs make_decode_args(const void* q, const void* kc, const void* vc, const int32_t* lens,
+                                 int B, int L, int Hq, int Hkv, float scale,
+                                 const DecodeShapeCheck& s, void* ws) {
+  gqa::DecodeArgs a;
+  a.q = (const uint16_t*)q;
+  a.kc = (const uint16_t*)kc;
+  a.vc = (const uint16_t*)vc;
+  a.lens = lens;
+  const size_t rows = (size_t)B * Hq * s.nsplit;
+  a.o_part = (float*)ws;
+  a.lse = (float*)((char*)ws + (rows * 128 * sizeof(float) + 255) / 256 * 256);
+  a.B = B; a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.hgroups = s.hgroups;
+  a.chunk = s.chunk;
+  a.nsplit = s.nsplit;
+  a.c = (float)((double)scale * kLog2e);
+  return a;
+}
+
+int run_decode(const void* q, const void* kc, const void* vc, const int32_t* lens, void* out,
+               int B, int L, int Hq, int Hkv, float scale, const DecodeShapeCheck& s,
+               void* ws, hipStream_t stream) {
+  gqa::DecodeArgs a = make_decode_args(q, kc, vc, lens, B, L, Hq, Hkv, scale, s, ws);
+  int e = gqa::launch_decode_split(a, stream);
+  if (e != 0) return hip_fail("decode split launch", e);
+  gqa::CombineArgs cmb{a.o_part, a.lse, (uint16_t*)out, B, Hq, s.nsplit};
+  e = gqa::launch_decode_combine(cmb, stream);
+  if (e != 0) return hip_fail("decode combine launch", e);
+  return GQA_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_attn_version(void) { return GQA_ATTN_VERSION; }
+
+const char* gqa_attn_strerror(int code) {
+  switch (code) {
+    case GQA_ATTN_OK: return "success";
+    case GQA_ATTN_ERR_NULL: return "a required pointer is NULL";
+    case GQA_ATTN_ERR_DIM: return "bad dimension or scale (sizes < 1, Hq % Hkv != 0, non-finite scale, or sizes too large)";
+    case GQA_ATTN_ERR_UNSUPPORTED: return "unsupported: head dim must be 128 and pointers 16-byte aligned";
+    case GQA_ATTN_ERR_HIP: return "HIP launch or allocation failure";
+    case GQA_ATTN_ERR_WORKSPACE: return "workspace missing or too small, or split size not a multiple of 64 in [64, 256]";
+    default: return "unknown error code";
+  }
+}
+
+const char* gqa_attn_last_error(void) { return g_last_error.c_str(); }
+
+int gqa_attn_prefill(const void* q, const void* k, const void* v, void* out,
+                     int B, int S, int Hq, int Hkv, int D, float scale, int causal,
+                     void* stream) {
+  if (!q || !k || !v || !out) return GQA_ATTN_ERR_NULL;
+  if (B < 1 || S < 1) return GQA_ATTN_ERR_DIM;
+  int e = check_heads(Hq, Hkv, D, scale);
+  if (e) return e;
+  if (elems4(B, S, Hq) < 0) return GQA_ATTN_ERR_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ATTN_ERR_UNSUPPORTED;
+  gqa::PrefillArgs a;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.out = (uint16_t*)out;
+  a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.nrb = (S + 31) / 32;
+  const long long units = (long long)a.G * a.nrb;
+  const long long wgs = (units + 3) / 4;
+  const long long grid = wgs * (long long)B * Hkv;
+  if (grid > 0x7fffffffLL) return GQA_ATTN_ERR_DIM;
+  a.wgs_per_slot = (int)wgs;
+  a.nslots = B * Hkv;
+  a.c = (float)((double)scale * kLog2e);
+  e = gqa::launch_prefill(a, causal != 0, (hipStream_t)stream);
+  if (e != 0) return hip_fail("prefill launch", e);
+  return GQA_ATTN_OK;
+}
+
+int gqa_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int* chunk, int* nsplit) {
+  DecodeShapeCheck s = check_decode_shape(B, L, Hq, Hkv, D, 1.0f, 0);
+  if (s.code) return s.code;
+  if (chunk) *chunk = s.chunk;
+  if (nsplit) *nsplit = s.nsplit;
+  return GQA_ATTN_OK;
+}
+
+size_t gqa_attn_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int D, int chunk) {
+  DecodeShapeCheck s = check_decode_shape(B, L, Hq, Hkv, D, 1.0f, chunk);
+  if (s.code) return 0;
+  return ws_bytes_for(B, Hq, s.nsplit);
+}
+
+int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
+                    const int32_t* lens, void* out,
+                    int B, int L, int Hq, int Hkv, int D, float scale,
+                    void* stream) {
+  if (!q || !kcache || !vcache || !lens || !out) return GQA_ATTN_ERR_NULL;
+  DecodeShapeCheck s = check_decode_shape(B, L, Hq, Hkv, D, scale, 0);
+  if (s.code) return s.code;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out))
+    return GQA_ATTN_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  int e = get_workspace(ws_bytes_for(B, Hq, s.nsplit), (hipStream_t)stream, &ws);
+  if (e) return e;
+  return run_decode(q, kcache, vcache, lens, out, B, L, Hq, Hkv, scale, s, ws, (hipStream_t)stream);
+}
+
+int gqa_attn_decode_ws(const void* q, const void* kcache, const void* vcache,
+                       const int32_t* lens, void* out,
+                       int B, int L, int Hq, int Hkv, int D, float scale,
+                       int chunk, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !kcache || !vcache || !lens || !out) return GQA_ATTN_ERR_NULL;
+  DecodeShapeCheck s = check_decode_shape(B, L, Hq, Hkv, D, scale, chunk);
+  if (s.code) return s.code;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out))
+    return GQA_ATTN_ERR_UNSUPPORTED;
+  if (!ws || !aligned16(ws) || ws_bytes < ws_bytes_for(B, Hq, s.nsplit)) return GQA_ATTN_ERR_WORKSPACE;
+  return run_decode(q, kcache, vcache, lens, out, B, L, Hq, Hkv, scale, s, ws, (hipStream_t)stream);
+}
+
+int gqa_attn_decode_partials(const void* q, const void* kcache, const void* vcache,
+                             const int32_t* lens, int B, int L, int Hq, int Hkv, int D,
+                             float scale, int chunk, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !kcache || !vcache || !lens) return GQA_ATTN_ERR_NULL;
+  DecodeShapeCheck s = check_decode_shape(B, L, Hq, Hkv, D, scale, chunk);
+  if (s.code) return s.code;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache)) return GQA_ATTN_ERR_UNSUPPORTED;
+  if (!ws || !aligned16(ws) || ws_bytes < ws_bytes_for(B, Hq, s.nsplit)) return GQA_ATTN_ERR_WORKSPACE;
+  gqa::DecodeArgs a = make_decode_args(q, kcache, vcache, lens, B, L, Hq, Hkv, scale, s, ws);
+  int e = gqa::launch_decode_split(a, (hipStream_t)stream);
+  if (e != 0) return hip_fail("decode split launch", e);
+  return GQA_ATTN_OK;
+}
+
+int gqa_attn_decode_combine(const void* ws, size_t ws_bytes, void* out,
+                            int B, int Hq, int D, int nsplit, void* stream) {
+  if (!ws || !out) return GQA_ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || nsplit < 1) return GQA_ATTN_ERR_DIM;
+  if (D != 128) return GQA_ATTN_ERR_UNSUPPORTED;
+  if (elems4(B, Hq, nsplit) < 0 || B > kMaxGridY || Hq > kMaxGridY) return GQA_ATTN_ERR_DIM;
+  if (!aligned16(ws) || !aligned16(out)) return GQA_ATTN_ERR_UNSUPPORTED;
+  if (ws_bytes < ws_bytes_for(B, Hq, nsplit)) return GQA_ATTN_ERR_WORKSPACE;
+  const size_t rows = (size_t)B * Hq * nsplit;
+  gqa::CombineArgs cmb{(const float*)ws,
+                       (const float*)((const char*)ws + (rows * 128 * sizeof(float) + 255) / 256 * 256),
+                       (uint16_t*)out, B, Hq, nsplit};
+  int e = gqa::launch_decode_combine(cmb, (hipStream_t)stream);
+  if (e != 0) return hip_fail("decode combine launch", e);
+  return GQA_ATTN_OK;
+}
+
+void gqa_attn_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if (g_ws.empty()) return;
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  for (auto& kv : g_ws) {
+    if (kv.second.ptr) {
+      (void)hipSetDevice(kv.first.first);
+      (void)hipFree(kv.second.ptr);
+    }
+  }
+  g_ws.clear();
+  (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// gqa_internal.hpp - kernel argument blocks and launch entry points shared between the
+// HIP kernel files and the C-ABI shim. Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+struct PrefillArgs {
+  const uint16_t* q;     // [B, S, Hq, D]
+  const uint16_t* k;     // [B, S, Hkv, D]
+  const uint16_t* v;     // [B, S, Hkv, D]
+  uint16_t* out;         // [B, S, Hq, D]
+  int B, S, Hq, Hkv, G;  // G = Hq / Hkv
+  int nrb;               // 32-row query blocks per sequence: ceil(S / 32)
+  int wgs_per_slot;      // workgroups per (b, kv head): ceil(G * nrb / 4)
+  int nslots;            // B * Hkv
+  float c;               // scale * log2(e)
+};
+
+struct DecodeArgs {
+  const uint16_t* q;     // [B, Hq, D]
+  const uint16_t* kc;    // [B, L, Hkv, D]
+  const uint16_t* vc;    // [B, L, Hkv, D]
+  const int32_t* lens;   // [B], device
+  float* o_part;         // [B, Hq, nsplit, D]
+  float* lse;            // [B, Hq, nsplit], log2 units
+  int B, L, Hq, Hkv, G;
+  int hgroups;           // ceil(G / 16): query heads are served 16 at a time
+  int chunk;             // keys per split, a multiple of 64
+  int nsplit;            // ceil(L / chunk)
+  float c;               // scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* o_part;
+  const float* lse;
+  uint16_t* out;         // [B, Hq, D]
+  int B, Hq, nsplit;
+};
+
+// Each returns a hipError_t value (0 = success) from the launch.
+int launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
+int launch_decode_split(const DecodeArgs& a, hipStream_t stream);
+int launch_decode_combine(const CombineArgs& a, hipStream_t stream);
+
+// Keys per split chosen for a decode of this shape (a multiple of 64).
+int decode_default_chunk(int B, int L, int Hkv, int G);
+// Largest supported keys per split.
+constexpr int kMaxChunk = 256;
+
+}  // namespace gqa

@@ -1,0 +1,239 @@
+// prefill.hip - causal / full GQA attention over a prompt on gfx950 (kernel K1).
+//
+// Implements the prefill mode of the chowfi/kernels README ("Result": process the full
+// prompt with a causal mask), with three of the ideas its "What helped most" section
+// lists, redone for CDNA4:
+//  - item 2 (GQA packing): the 4 waves of a workgroup are the query heads of one KV
+//    group (or, for other group sizes, consecutive row blocks), so each K/V tile is
+//    staged once into LDS and read by every head that shares it;
+//  - item 3 (skip the masked half): a workgroup stops at the last key tile its rows can
+//    see, and a wave skips the arithmetic of tiles that lie wholly above its diagonal;
+//  - item 4 (largest blocks first): workgroup ids are mapped so the query tiles with the
+//    most key tiles start first;
+//  - item 5 (exp2 math): the softmax runs in base 2 with scale*log2(e) folded into the
+//    logits, on the native v_exp_f32.
+//
+// Work decomposition. One wave owns 32 query rows of one head and keeps, per lane, one
+// query row (lane % 32) and half of the keys of every tile (lane / 32). Scores are
+// computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K from LDS is the A
+// operand, the wave's Q rows stay in registers as the B operand. In that layout each
+// lane's 32 scores of a 64-key tile belong to its own query row, so the row max needs
+// only one exchange between the two wave halves. The probabilities are rounded to bf16
+// in place and fed, with no data movement, as the B operand of O^T += V^T P^T; V^T comes
+// from LDS through ds_read_b64_tr_b16.
+//
+// Online softmax (per query row, fp32): running max m (log2 units), partial sum l, and
+// the accumulator O. The rescale of O is lazy: m only moves when a tile raises the row
+// max by more than kTau, so most tiles skip the 64 multiplies; numerator and denominator
+// always share the same m, so the result is unchanged.
+#include "gqa_device.hpp"
+#include "gqa_internal.hpp"
+
+namespace gqa {
+
+constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 units (p <= 2^8)
+
+template <bool CAUSAL, bool POS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[kTileBytes];
+  GQA_LDS uint8_t* const K0 = (GQA_LDS uint8_t*)lds_k0;
+  GQA_LDS uint8_t* const V0 = (GQA_LDS uint8_t*)lds_v0;
+  GQA_LDS uint8_t* const K1 = (GQA_LDS uint8_t*)lds_k1;
+  GQA_LDS uint8_t* const V1 = (GQA_LDS uint8_t*)lds_v1;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;      // which half of every 64-key tile this lane holds
+  const int qi = lane & 31;     // this lane's query row within the wave's 32 rows
+
+  // Workgroup -> (batch, KV head, query tile). Consecutive ids go to different (b, g)
+  // slots; with 8 KV heads and round-robin dispatch over 8 XCDs each XCD then serves one
+  // KV head, whose K/V stays in that XCD's L2. Within a slot, ids run over query tiles
+  // from the last (most key tiles) to the first.
+  const int bid = blockIdx.x;
+  const int slot = bid % a.nslots;
+  const int j = bid / a.nslots;
+  const int wg = CAUSAL ? (a.wgs_per_slot - 1 - j) : j;
+  const int b = slot / a.Hkv;
+  const int g = slot % a.Hkv;
+  const int nunits = a.G * a.nrb;
+  const int unit = 4 * wg + wave;
+  const bool active = unit < nunits;
+  const int rb = active ? unit / a.G : 0;
+  const int head = g * a.G + (active ? unit % a.G : 0);
+  const int q0 = rb * 32;
+
+  const int last_unit = min(4 * wg + 3, nunits - 1);
+  const int kv_end = CAUSAL ? min(a.S, (last_unit / a.G) * 32 + 32) : a.S;
+  const int nt = (kv_end + kTileRows - 1) / kTileRows;
+  const int own_end = CAUSAL ? min(a.S, q0 + 32) : a.S;
+  const int own_nt = (own_end + kTileRows - 1) / kTileRows;
+
+  const size_t kv_stride = (size_t)a.Hkv * kD;
+  const uint16_t* kbase = a.k + ((size_t)b * a.S * a.Hkv + g) * kD;
+  const uint16_t* vbase = a.v + ((size_t)b * a.S * a.Hkv + g) * kD;
+
+  // Prologue: start tile 0, then fetch this wave's Q rows (B operand, 8 k-steps of 16 d).
+  stage_tile<4, false>(K0, kbase, kv_stride, kv_end, wave, lane);
+  stage_tile<4, true>(V0, vbase, kv_stride, kv_end, wave, lane);
+  bf16x8 qreg[8];
+  {
+    const int qrow = min(q0 + qi, a.S - 1);
+    const uint16_t* qp = a.q + (((size_t)b * a.S + qrow) * a.Hq + head) * kD + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qreg[ks] = *(const bf16x8*)(qp + 16 * ks);
+  }
+  // Q and tile 0 have landed. Waiting here also tells the compiler that no load of its
+  // own is outstanding inside the loop, so it adds no waits there.
+  wait_vmcnt<0>();
+
+  const float c = a.c;
+  float m_run = -INFINITY;
+  float l_part = 0.f;
+  f32x16 oacc[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) oacc[mb] = f32x16{};
+
+  // One key tile. BUF selects the LDS buffers at compile time, so every LDS access
+  // names one __shared__ array and the copies into the other buffer are known not to
+  // alias the reads of this one.
+  auto step = [&](int t, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    GQA_LDS uint8_t* const kt = BUF ? K1 : K0;
+    GQA_LDS uint8_t* const vt = BUF ? V1 : V0;
+    GQA_LDS uint8_t* const kn = BUF ? K0 : K1;
+    GQA_LDS uint8_t* const vn = BUF ? V0 : V1;
+    // Every wave is done with the buffers of tile t-1 (kn/vn) before they are refilled:
+    // its LDS reads of them fed MFMAs that have issued, so they have completed.
+    tile_barrier();
+    if (t + 1 < nt) {
+      const int r0 = (t + 1) * kTileRows;
+      stage_tile<4, false>(kn, kbase + (size_t)r0 * kv_stride, kv_stride, kv_end - r0, wave, lane);
+      stage_tile<4, true>(vn, vbase + (size_t)r0 * kv_stride, kv_stride, kv_end - r0, wave, lane);
+      wait_vmcnt<8>();   // this wave's copies of tile t have landed (8 of t+1 may remain)
+    } else {
+      wait_vmcnt<0>();
+    }
+    tile_barrier();      // ... and so have every other wave's
+    if (!active || t >= own_nt) return;
+
+    // S^T[key][query] for the tile's 64 keys, two 32-key blocks.
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 a0 = lds_read_k(kt, qi, 2 * ks + h);
+      const bf16x8 a1 = lds_read_k(kt, 32 + qi, 2 * ks + h);
+      s0 = mfma32(a0, qreg[ks], s0);
+      s1 = mfma32(a1, qreg[ks], s1);
+    }
+    if (!POS) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) { s0[v] *= c; s1[v] *= c; }
+    }
+    // Mask keys this lane's query may not see: above the diagonal (causal) or past S.
+    const int key0 = t * kTileRows;
+    const bool need_mask = CAUSAL ? (key0 + kTileRows - 1 > q0) : (key0 + kTileRows > a.S);
+    if (need_mask) {
+      const int lim = CAUSAL ? (q0 + qi) : (a.S - 1);   // largest visible key
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kk = key0 + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (kk > lim) s0[v] = -INFINITY;
+        if (kk + 32 > lim) s1[v] = -INFINITY;
+      }
+    }
+    float mx = s0[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s0[v]);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s1[v]);
+    mx = halves_max(mx);
+    const float m_cand = fmaxf(m_run, POS ? mx * c : mx);
+    const bool upd = m_cand > m_run + kTau;
+    if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+      const float m_new = upd ? m_cand : m_run;
+      const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) oacc[mb] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = -m_run;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      s0[v] = exp2_fast(POS ? __builtin_fmaf(s0[v], c, neg_m) : s0[v] + neg_m);
+      s1[v] = exp2_fast(POS ? __builtin_fmaf(s1[v], c, neg_m) : s1[v] + neg_m);
+    }
+    // P^T as the B operand of O^T = V^T P^T: 4 k-steps of 16 keys, straight from the
+    // accumulator layout (k index 8h+u <-> key 16t4 + 8(u/4) + 4h + u%4).
+    bf16x8 p[4];
+    p[0] = to_bf16x8(s0[0], s0[1], s0[2], s0[3], s0[4], s0[5], s0[6], s0[7]);
+    p[1] = to_bf16x8(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
+    p[2] = to_bf16x8(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
+    p[3] = to_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) l_part = sum_bf16x8(p[t4], l_part);
+
+    // O^T[d][query] += V^T[d][key] P^T[key][query]. The A operand for d-block mb and
+    // k-step t4: lane l holds d = 32mb + l%32 and keys 16t4 + 4(l/32) + {0..3, 8..11}.
+    const int g16 = lane >> 4;
+    const int li = lane & 15;
+    const int vrow = 4 * (g16 >> 1) + (li >> 2);
+    const int vcol = 16 * (g16 & 1) + 4 * (li & 3);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const s16x4 lo = lds_read_v_tr(vt, 16 * t4 + vrow, 32 * mb + vcol);
+        const s16x4 hi = lds_read_v_tr(vt, 16 * t4 + 8 + vrow, 32 * mb + vcol);
+        oacc[mb] = mfma32(join_bf16x8(lo, hi), p[t4], oacc[mb]);
+      }
+    }
+  };
+
+  for (int t = 0; t < nt; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < nt) step(t + 1, std::integral_constant<int, 1>{});
+  }
+
+  // Epilogue: the two halves of the wave hold disjoint keys of the same rows.
+  const float l_tot = halves_sum(l_part);
+  if (!active) return;
+  const int qpos = q0 + qi;
+  if (qpos >= a.S) return;
+  const float inv = 1.0f / l_tot;
+  uint16_t* op = a.out + (((size_t)b * a.S + qpos) * a.Hq + head) * kD + 4 * h;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq) {
+      typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+      u16x4 w;
+      w[0] = bf16_bits(oacc[mb][4 * vq + 0] * inv);
+      w[1] = bf16_bits(oacc[mb][4 * vq + 1] * inv);
+      w[2] = bf16_bits(oacc[mb][4 * vq + 2] * inv);
+      w[3] = bf16_bits(oacc[mb][4 * vq + 3] * inv);
+      *(u16x4*)(op + 32 * mb + 8 * vq) = w;
+    }
+  }
+}
+
+int launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream) {
+  const dim3 grid((unsigned)((size_t)a.nslots * a.wgs_per_slot));
+  const dim3 block(256);
+  const bool pos = a.c > 0.f;
+  if (causal) {
+    if (pos) hipLaunchKernelGGL((prefill_kernel<true, true>), grid, block, 0, stream, a);
+    else     hipLaunchKernelGGL((prefill_kernel<true, false>), grid, block, 0, stream, a);
+  } else {
+    if (pos) hipLaunchKernelGGL((prefill_kernel<false, true>), grid, block, 0, stream, a);
+    else     hipLaunchKernelGGL((prefill_kernel<false, false>), grid, block, 0, stream, a);
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace gqa

@@ -1,0 +1,159 @@
+/*
+ * gqa_attn.h - C ABI of the MI355X (gfx950) grouped-query attention forward library.
+ *
+ * The library computes the forward pass of grouped-query attention (GQA) in its
+ * two modes: causal prefill over a full prompt and single-token decode against a
+ * KV cache (chowfi/kernels README, "Result": the two mode bullets and the
+ * settings line, bf16 with 32 query heads sharing 8 KV heads of size 128).
+ *
+ * Definition (the page names the operation but writes no formula; it is
+ * benchmarked as the same function as FlashAttention-2 and PyTorch SDPA, so the
+ * standard one is taken). For batch b, query head h and KV head g(h) = h / (Hq/Hkv):
+ *     x[i,j]    = scale * dot(Q[b,i,h,:], K[b,j,g(h),:])       for visible j
+ *     out[i,:]  = sum_j softmax_j(x[i,:]) * V[b,j,g(h),:]
+ * Prefill, causal: query i sees keys 0..i. Prefill, non-causal: keys 0..S-1.
+ * Decode: the one query of sequence b sees cache slots 0..lens[b]-1.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are contiguous, device-resident and 16-byte aligned. bf16 values
+ *    are passed as raw uint16 bit patterns. The caller owns every tensor.
+ *  - Only D = 128 is supported. Hq must be a multiple of Hkv.
+ *  - Arithmetic: bf16 operands into matrix cores with fp32 accumulation; the
+ *    softmax max, sum and the output accumulator are fp32; outputs are rounded
+ *    to bf16 (round to nearest even).
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    on that stream only and calls return without a host synchronisation. A
+ *    fault inside a kernel surfaces at the caller's next synchronisation.
+ *  - Arguments are validated before any HIP call, so every error code below
+ *    except GQA_ATTN_ERR_HIP can be produced on a machine without a GPU.
+ *  - Results are bitwise deterministic for a fixed shape, scale and split
+ *    count: no reduction uses atomics.
+ *  - Entry points may be called from several host threads. Calls that share
+ *    a stream are ordered by that stream.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define GQA_ATTN_OK               0
+#define GQA_ATTN_ERR_NULL        -1  /* a required pointer is NULL                                  */
+#define GQA_ATTN_ERR_DIM         -2  /* B, S, L, Hq or Hkv < 1; Hq % Hkv != 0; non-finite scale;
+                                        a size whose element count overflows 64-bit offsets         */
+#define GQA_ATTN_ERR_UNSUPPORTED -3  /* D != 128, or a pointer that is not 16-byte aligned          */
+#define GQA_ATTN_ERR_HIP         -4  /* a HIP launch or allocation failed (see gqa_attn_last_error) */
+#define GQA_ATTN_ERR_WORKSPACE   -5  /* caller workspace NULL/too small, or a bad split size        */
+
+/*
+ * Causal (or full) attention over a prompt.
+ *   q, out : [B, S, Hq, D]  bf16
+ *   k, v   : [B, S, Hkv, D] bf16
+ *   scale  : logit scale (callers normally pass 1/sqrt(D)); any finite value.
+ *   causal : nonzero = query i sees keys 0..i; zero = every query sees all S keys.
+ * Implements the prefill mode (chowfi/kernels README, "Result": prefill processes
+ * the full prompt with a causal mask). Whole key tiles above the diagonal are
+ * never visited ("What helped most", item 3), and the query tiles with the most
+ * key tiles are launched first (item 4).
+ * Allocates nothing.
+ */
+int gqa_attn_prefill(const void* q, const void* k, const void* v, void* out,
+                     int B, int S, int Hq, int Hkv, int D, float scale, int causal,
+                     void* stream);
+
+/*
+ * One-token decode against a KV cache, split along the cache.
+ *   q, out         : [B, Hq, D]  bf16
+ *   kcache, vcache : [B, L, Hkv, D] bf16; L is the capacity (the row stride).
+ *   lens           : device int32 [B]. Sequence b attends slots 0..lens[b]-1.
+ *                    Values are clamped to [0, L] in the kernel and never read
+ *                    on the host. lens[b] = 0 gives a zero output row. Slots at
+ *                    or past lens[b] are never read, whatever they hold.
+ * Implements the decode mode ("Result": decode generates one token from a KV
+ * cache of a given length). The cache is cut into chunks that run in parallel
+ * on all CUs and are then merged by a log-sum-exp combine ("What helped most",
+ * item 1). Each chunk's K/V rows are read once for all query heads of their
+ * group (item 2).
+ * The split partials live in a library-owned workspace, cached per device and
+ * grown on demand (one hipMalloc the first time a larger size is needed on a
+ * device; none afterwards). The workspace is not shared across streams: each
+ * (device, stream) pair gets its own, so concurrent streams never race.
+ */
+int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
+                    const int32_t* lens, void* out,
+                    int B, int L, int Hq, int Hkv, int D, float scale,
+                    void* stream);
+
+/*
+ * The split the library would choose for a decode of this shape.
+ * On success writes the keys per split (*chunk, a multiple of 64) and the
+ * number of splits (*nsplit = ceil(L / chunk)). Either output may be NULL.
+ */
+int gqa_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int* chunk, int* nsplit);
+
+/*
+ * Bytes of workspace a decode needs with `chunk` keys per split (0 = the
+ * library's own choice). Returns 0 if the arguments are invalid.
+ * Layout: fp32 o_part[B][Hq][nsplit][D], then fp32 lse[B][Hq][nsplit].
+ */
+size_t gqa_attn_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int D, int chunk);
+
+/*
+ * Decode with a caller-owned workspace and an explicit split size. Same
+ * semantics as gqa_attn_decode. chunk = 0 takes the library's choice;
+ * otherwise chunk must be a positive multiple of 64. ws must be 16-byte
+ * aligned and hold at least gqa_attn_decode_workspace_bytes(..., chunk) bytes.
+ * Allocates nothing.
+ */
+int gqa_attn_decode_ws(const void* q, const void* kcache, const void* vcache,
+                       const int32_t* lens, void* out,
+                       int B, int L, int Hq, int Hkv, int D, float scale,
+                       int chunk, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The first half of a decode on its own: per-split partial results.
+ * Writes, for every (b, h, split s) with chunk keys per split:
+ *   o_part[b][h][s][:] (fp32, the chunk's softmax-weighted mean of V) and
+ *   lse[b][h][s]       (fp32, log2 of sum_j 2^(x_j * log2(e)) over the chunk,
+ *                       i.e. the chunk's log-sum-exp in base-2 units;
+ *                       -inf for an empty chunk; such a chunk's o_part row is not
+ *                       written and must be ignored).
+ * ws is laid out as in gqa_attn_decode_workspace_bytes. Allocates nothing.
+ */
+int gqa_attn_decode_partials(const void* q, const void* kcache, const void* vcache,
+                             const int32_t* lens, int B, int L, int Hq, int Hkv, int D,
+                             float scale, int chunk, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The second half of a decode on its own: log-sum-exp merge of nsplit
+ * partials (laid out as above) into out [B, Hq, D] bf16. A row whose every
+ * split is empty becomes zero. Allocates nothing.
+ */
+int gqa_attn_decode_combine(const void* ws, size_t ws_bytes, void* out,
+                            int B, int Hq, int D, int nsplit, void* stream);
+
+/* Static description of a return code. Never NULL. */
+const char* gqa_attn_strerror(int code);
+
+/* Detail of the most recent GQA_ATTN_ERR_HIP on the calling thread ("" if none). */
+const char* gqa_attn_last_error(void);
+
+/* Frees the library-cached decode workspaces. The caller must ensure no decode
+ * using them is still in flight (for example by synchronising the device). */
+void gqa_attn_release(void);
+
+/* ABI version of this header. */
+int gqa_attn_version(void);
+
+#define GQA_ATTN_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

@@ -1,0 +1,51 @@
+"""Shared helpers for the GPU parity tests: device transfer and error measures.
+
+The tolerance is the one the workload states for a bf16 output compared with
+an fp64 reference: max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3,
+over every compared element.
+"""
+
+import numpy as np
+import torch
+
+import oracle
+from gqa_inputs import bf16_bits
+
+TOL_MAX = 2e-2
+TOL_MEAN = 2e-3
+
+
+def dev(t: torch.Tensor) -> torch.Tensor:
+    return t.to("cuda:0").contiguous()
+
+
+def gpu_f64(t: torch.Tensor) -> np.ndarray:
+    """bf16 GPU tensor -> float64 numpy (exact)."""
+    return oracle.bf16_bits_to_f64(bf16_bits(t))
+
+
+def errors(got: np.ndarray, want: np.ndarray):
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.all(np.isfinite(got)), "non-finite values in the GPU output"
+    d = np.abs(got - want)
+    return float(d.max()), float(d.mean())
+
+
+def assert_close(got: np.ndarray, want: np.ndarray, what: str = ""):
+    mx, mean = errors(got, want)
+    floor_mx, floor_mean = errors(oracle.round_to_bf16(want), want)
+    msg = (f"{what}: max abs err {mx:.3e} (tol {TOL_MAX}), mean {mean:.3e} (tol {TOL_MEAN}); "
+           f"bf16 rounding floor max {floor_mx:.3e} mean {floor_mean:.3e}")
+    print(msg, flush=True)
+    assert mx <= TOL_MAX and mean <= TOL_MEAN, msg
+    return mx, mean
+
+
+def sample_rows(S: int, extra: int = 16, seed: int = 0):
+    """Query rows to check at full size: both ends, tile and wave boundaries, the middle,
+    plus a few random ones."""
+    base = [0, 1, 31, 32, 33, 63, 64, 65, 127, 128, S // 2 - 1, S // 2, S - 65, S - 64,
+            S - 33, S - 32, S - 2, S - 1]
+    rng = np.random.default_rng(seed)
+    rnd = rng.integers(0, S, size=extra).tolist()
+    return sorted({r for r in base + rnd if 0 <= r < S})

@@ -1,0 +1,131 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library must load, export every function include/gqa_attn.h declares, and
+reject bad arguments with the documented codes before it makes any HIP call.
+All pointers passed here are fake (never dereferenced): each call fails
+validation before anything would touch them.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gqa_flash_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+
+P = 0x10000      # a fake, 16-byte aligned "device pointer"
+MIS = 0x10008    # a fake pointer that is not 16-byte aligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.get()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_attn_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror(lib):
+    assert lib.gqa_attn_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -99):
+        s = lib.gqa_attn_strerror(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.gqa_attn_last_error() == b""
+
+
+def _prefill(lib, q=P, k=P, v=P, o=P, B=1, S=16, Hq=32, Hkv=8, D=128, scale=0.088, causal=1):
+    return lib.gqa_attn_prefill(q, k, v, o, B, S, Hq, Hkv, D, scale, causal, None)
+
+
+def test_prefill_argument_errors(lib):
+    assert _prefill(lib, q=None) == _lib.ERR_NULL
+    assert _prefill(lib, o=None) == _lib.ERR_NULL
+    assert _prefill(lib, B=0) == _lib.ERR_DIM
+    assert _prefill(lib, S=0) == _lib.ERR_DIM
+    assert _prefill(lib, S=-5) == _lib.ERR_DIM
+    assert _prefill(lib, Hq=0) == _lib.ERR_DIM
+    assert _prefill(lib, Hkv=0) == _lib.ERR_DIM
+    assert _prefill(lib, Hq=30, Hkv=8) == _lib.ERR_DIM
+    assert _prefill(lib, scale=float("nan")) == _lib.ERR_DIM
+    assert _prefill(lib, scale=float("inf")) == _lib.ERR_DIM
+    assert _prefill(lib, D=64) == _lib.ERR_UNSUPPORTED
+    assert _prefill(lib, D=256) == _lib.ERR_UNSUPPORTED
+    assert _prefill(lib, q=MIS) == _lib.ERR_UNSUPPORTED
+    assert _prefill(lib, v=MIS) == _lib.ERR_UNSUPPORTED
+    assert _prefill(lib, o=MIS) == _lib.ERR_UNSUPPORTED
+    # element counts past 2^62 are refused rather than wrapped
+    assert _prefill(lib, B=2 ** 30, S=2 ** 30) == _lib.ERR_DIM
+
+
+def _decode(lib, q=P, k=P, v=P, lens=P, o=P, B=1, L=64, Hq=32, Hkv=8, D=128, scale=0.088):
+    return lib.gqa_attn_decode(q, k, v, lens, o, B, L, Hq, Hkv, D, scale, None)
+
+
+def test_decode_argument_errors(lib):
+    assert _decode(lib, lens=None) == _lib.ERR_NULL
+    assert _decode(lib, k=None) == _lib.ERR_NULL
+    assert _decode(lib, B=0) == _lib.ERR_DIM
+    assert _decode(lib, L=0) == _lib.ERR_DIM
+    assert _decode(lib, Hq=12, Hkv=8) == _lib.ERR_DIM
+    assert _decode(lib, scale=float("-inf")) == _lib.ERR_DIM
+    assert _decode(lib, B=70000) == _lib.ERR_DIM          # grid z limit
+    assert _decode(lib, D=96) == _lib.ERR_UNSUPPORTED
+    assert _decode(lib, q=MIS) == _lib.ERR_UNSUPPORTED
+    assert _decode(lib, k=MIS) == _lib.ERR_UNSUPPORTED
+
+
+def test_decode_ws_and_split_errors(lib):
+    need = lib.gqa_attn_decode_workspace_bytes(1, 1000, 32, 8, 128, 128)
+    assert need > 0
+    base = dict(q=P, k=P, v=P, lens=P, o=P)
+
+    def call(chunk=128, ws=P, ws_bytes=need):
+        return lib.gqa_attn_decode_ws(base["q"], base["k"], base["v"], base["lens"], base["o"],
+                                      1, 1000, 32, 8, 128, 0.088, chunk, ws, ws_bytes, None)
+    assert call(ws=None) == _lib.ERR_WORKSPACE
+    assert call(ws=MIS) == _lib.ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == _lib.ERR_WORKSPACE
+    for bad in (1, 63, 100, 320, -64):
+        assert call(chunk=bad) == _lib.ERR_WORKSPACE, bad
+    assert lib.gqa_attn_decode_workspace_bytes(1, 1000, 32, 8, 128, 100) == 0
+    rc = lib.gqa_attn_decode_partials(P, P, P, P, 1, 1000, 32, 8, 128, 0.088, 128, P, need - 1, None)
+    assert rc == _lib.ERR_WORKSPACE
+    rc = lib.gqa_attn_decode_combine(P, 10, P, 1, 32, 128, 8, None)
+    assert rc == _lib.ERR_WORKSPACE
+    assert lib.gqa_attn_decode_combine(None, 10, P, 1, 32, 128, 8, None) == _lib.ERR_NULL
+    assert lib.gqa_attn_decode_combine(P, 10 ** 9, P, 1, 32, 64, 8, None) == _lib.ERR_UNSUPPORTED
+    assert lib.gqa_attn_decode_combine(P, 10 ** 9, P, 1, 32, 128, 0, None) == _lib.ERR_DIM
+
+
+def test_decode_plan_and_workspace_size(lib):
+    chunk = ctypes.c_int(0)
+    nsplit = ctypes.c_int(0)
+    for L in (1, 63, 64, 2048, 16384, 65536, 50001):
+        assert lib.gqa_attn_decode_plan(1, L, 32, 8, 128, ctypes.byref(chunk), ctypes.byref(nsplit)) == 0
+        assert chunk.value % 64 == 0 and 64 <= chunk.value <= 256
+        assert nsplit.value == -(-L // chunk.value)
+        ws = lib.gqa_attn_decode_workspace_bytes(1, L, 32, 8, 128, 0)
+        rows = 32 * nsplit.value
+        assert ws == (rows * 128 * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
+    assert lib.gqa_attn_decode_plan(1, 100, 32, 8, 128, None, None) == 0
+    assert lib.gqa_attn_decode_plan(0, 100, 32, 8, 128, None, None) == _lib.ERR_DIM
+
+
+def test_release_without_any_workspace_is_harmless(lib):
+    lib.gqa_attn_release()
