@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Throughput of the GQA attention forward hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+a causal prefill (B=1, S=32768, 32 query heads / 8 KV heads, d=128, bf16),
+then a one-token decode against a KV cache of L=65536 (same heads) -- the
+largest prefill and decode sizes of the workload (chowfi/kernels README,
+"Result" table: prefill 2K..32K, decode 2K..64K).
+
+Printed (rank 0, one JSON line): the contract fields, with
+- value      : causal prefill TFLOP/s (FLOPs = 2*2*S*(S+1)/2*Hq*D, the causal half);
+- decode     : decode KV-read GB/s (bytes = K+V read once = 2*L*Hkv*D*2, plus q and out);
+- roofline   : the prefill kernel against the bf16 dense MFMA peak (it is most of the step);
+- roofline_decode : the decode kernels against the HBM peak;
+- cpu_baseline: the fp64 CPU oracle on a bounded sample of the same prefill.
+Kernel durations come from HIP events recorded on the stream the kernels run on,
+inside the timed region. The prefill streams ~671 MB between decodes, which flushes
+the 256 MB MALL, so every decode reads its cache from HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --sweep out.jsonl     # every prefill/decode size, one JSON line each
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HQ, HKV, D = 32, 8, 128
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+METRIC = "causal prefill TFLOP/s + decode KV-read GB/s (GQA 32q/8kv d128 bf16, 1 GPU)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def prefill_flops(S: int, B: int = 1) -> float:
+    return 2.0 * 2.0 * S * (S + 1) / 2.0 * HQ * D * B
+
+
+def decode_bytes(L_total: int, B: int = 1) -> float:
+    """K+V read once per KV head for L_total cached tokens, plus q and out."""
+    return 2.0 * L_total * HKV * D * 2 + 2.0 * B * HQ * D * 2
+
+
+def kernel_sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gqa_flash_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if taken on the current sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_digest") != kernel_sources_digest():
+        return None
+    entry = t.get("kernels", {}).get(kernel_key)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+def make_inputs(S: int, L: int, dev):
+    import torch
+    from gqa_inputs import decode_inputs, prefill_inputs, seed_base
+    q, k, v = prefill_inputs(1, S, base=seed_base(2, 4))
+    qd, kc, vc, lens = decode_inputs(1, L, base=seed_base(1, 5))
+    t = [x.to(dev) for x in (q, k, v, qd, kc, vc, lens)]
+    torch.cuda.synchronize()
+    return t
+
+
+def cpu_baseline(S: int, budget_s: float = 15.0):
+    """Time the fp64 oracle on contiguous 256-row blocks of the S-token causal prefill,
+    spread evenly over the sequence, until about budget_s seconds have been spent."""
+    import numpy as np
+    import oracle
+    from gqa_inputs import bf16_bits, prefill_inputs, seed_base
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    q, k, v = prefill_inputs(1, S, base=seed_base(2, 4))
+    qb, kb, vb = bf16_bits(q), bf16_bits(k), bf16_bits(v)
+    blocks = 256
+    order = []
+    nblk = S // blocks
+    # visit blocks in a stride order that covers early, late and middle positions evenly
+    step = max(1, nblk // 16)
+    for off in range(step):
+        order.extend(range(off, nblk, step))
+    flops = 0.0
+    rows_done = 0
+    spent = 0.0
+    for bi in order:
+        r0 = bi * blocks
+        rows = np.arange(r0, r0 + blocks)
+        t0 = time.perf_counter()
+        oracle.prefill(qb, kb, vb, causal=True, rows=rows)
+        spent += time.perf_counter() - t0
+        flops += float(np.sum(4.0 * (rows + 1) * D * HQ))
+        rows_done += blocks
+        if spent >= budget_s:
+            break
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle, causal prefill S={S} B=1 Hq={HQ} Hkv={HKV} D={D}: "
+                   f"{rows_done} query rows (all heads) in 256-row blocks spread over the sequence, "
+                   f"{flops / 1e9:.1f} GFLOP algorithmic in {spent:.1f} s"),
+    }
+
+
+def run_step_timing(S, L, steps, warmup):
+    import torch
+    import gqa_flash_attention_amd as gqa
+    dev = torch.device("cuda:0")
+    q, k, v, qd, kc, vc, lens = make_inputs(S, L, dev)
+    out_p = torch.empty_like(q)
+    out_d = torch.empty_like(qd)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gqa.prefill(q, k, v, causal=True, out=out_p)
+        gqa.decode(qd, kc, vc, lens, out=out_d)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        gqa.prefill(q, k, v, causal=True, out=out_p)
+        ev[i][1].record(stream)
+        gqa.decode(qd, kc, vc, lens, out=out_d)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pf = sorted(ev[i][0].elapsed_time(ev[i][1]) for i in range(steps))
+    dc = sorted(ev[i][1].elapsed_time(ev[i][2]) for i in range(steps))
+    return wall, pf, dc
+
+
+def main_line(args):
+    import torch
+    S, L = args.prefill_s, args.decode_l
+    wall, pf, dc = run_step_timing(S, L, args.steps, args.warmup)
+    pf_mean = sum(pf) / len(pf)
+    dc_mean = sum(dc) / len(dc)
+    fl = prefill_flops(S)
+    by = decode_bytes(L)
+    value = fl / (pf_mean * 1e-3) / 1e12
+    dec_gbs = by / (dc_mean * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 activations; no dataset)",
+        "config": {
+            "workload": f"GQA forward, Llama-3-8B attention shape: causal prefill S={S} + decode L={L}, B=1",
+            "B": 1, "Hq": HQ, "Hkv": HKV, "D": D, "prefill_S": S, "decode_L": L,
+        },
+        "decode": {
+            "value": round(dec_gbs, 1), "unit": "GB/s",
+            "ms": round(dc_mean, 5), "ms_min": round(dc[0], 5), "ms_median": round(dc[len(dc) // 2], 5),
+            "bytes": by,
+        },
+        "prefill": {
+            "ms": round(pf_mean, 4), "ms_min": round(pf[0], 4), "ms_median": round(pf[len(pf) // 2], 4),
+            "flops": fl,
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(value / PEAK_BF16_TFLOPS, 4),
+            "traffic": load_traffic(f"prefill_S{S}"),
+            "kernel": "prefill_kernel<causal>",
+        },
+        "roofline_decode": {
+            "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic(f"decode_L{L}"),
+            "kernel": "decode_split_kernel + decode_combine_kernel",
+        },
+        "device": torch.cuda.get_device_name(0),
+    }
+    if args.cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(S, budget_s=args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+def sweep(path, steps, warmup):
+    """Every prefill and decode size of the workload, each timed on its own (events per call).
+    Decode caches are rotated through >= 1 GB of distinct copies so the MALL holds none."""
+    import torch
+    import gqa_flash_attention_amd as gqa
+    from gqa_inputs import decode_inputs, prefill_inputs, seed_base
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+
+    def timed(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            evs[i][0].record(stream)
+            fn(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs)
+
+    for S in (512, 2048, 4096, 8192, 16384, 32768):
+        q, k, v = [x.to(dev) for x in prefill_inputs(1, S, base=seed_base(2, 0))]
+        out = torch.empty_like(q)
+        for _ in range(warmup):
+            gqa.prefill(q, k, v, out=out)
+        ms = timed(lambda i: gqa.prefill(q, k, v, out=out), steps)
+        med = ms[len(ms) // 2]
+        r = {"mode": "prefill", "S": S, "ms_median": med, "ms_min": ms[0],
+             "tflops": prefill_flops(S) / (med * 1e-3) / 1e12}
+        r["frac_of_peak"] = r["tflops"] / PEAK_BF16_TFLOPS
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+        del q, k, v, out
+    for L in (2048, 4096, 8192, 16384, 32768, 65536):
+        per = L * HKV * D * 2 * 2
+        ncopies = max(2, min(64, -(-(1 << 30) // per)))
+        qd, kc, vc, lens = decode_inputs(1, L, base=seed_base(1, 0))
+        qd, lens = qd.to(dev), lens.to(dev)
+        kcs = [kc.to(dev) for _ in range(ncopies)]
+        vcs = [vc.to(dev) for _ in range(ncopies)]
+        out = torch.empty_like(qd)
+        for i in range(warmup):
+            gqa.decode(qd, kcs[i % ncopies], vcs[i % ncopies], lens, out=out)
+        ms = timed(lambda i: gqa.decode(qd, kcs[i % ncopies], vcs[i % ncopies], lens, out=out), max(steps, 2 * ncopies))
+        med = ms[len(ms) // 2]
+        r = {"mode": "decode", "L": L, "ms_median": med, "ms_min": ms[0], "copies_rotated": ncopies,
+             "gbs": decode_bytes(L) / (med * 1e-3) / 1e9}
+        r["frac_of_peak"] = r["gbs"] / PEAK_HBM_GBS
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+        del kcs, vcs
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        for r in rows:
+            f.write(json.dumps(r) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prefill-s", type=int, default=32768)
+    ap.add_argument("--decode-l", type=int, default=65536)
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU baseline")
+    ap.add_argument("--sweep", metavar="OUT_JSONL", default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(the attention hot path here runs on a single MI355X). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.sweep:
+        sweep(args.sweep, args.steps, args.warmup)
+    else:
+        main_line(args)
+
+
+if __name__ == "__main__":
+    main()
