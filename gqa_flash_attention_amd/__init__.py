@@ -95,7 +95,9 @@ def decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, lens: to
 
     With neither ``chunk`` nor ``workspace`` the library picks the split and uses
     its own cached workspace; otherwise a torch-owned workspace is used (allocated
-    here if not given) with the requested keys per split.
+    here, zeroed, if not given) with the requested keys per split. A workspace
+    passed in must have been allocated zeroed (its leading merge counters must be
+    zero; every completed call leaves them zero).
     """
     B, L, Hq, Hkv, D = _check_decode(q, kcache, vcache, lens)
     if out is None:
@@ -115,7 +117,8 @@ def decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, lens: to
     ch = 0 if chunk is None else int(chunk)
     need = lib.gqa_attn_decode_workspace_bytes(B, L, Hq, Hkv, D, ch)
     if workspace is None:
-        workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=q.device)
+        # zeroed: the merge counters at the end of the workspace must start at zero
+        workspace = torch.zeros(max(int(need), 16), dtype=torch.uint8, device=q.device)
     rc = lib.gqa_attn_decode_ws(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), lens.data_ptr(),
                                 out.data_ptr(), B, L, Hq, Hkv, D, float(scale), ch,
                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -138,10 +141,12 @@ def decode_workspace_bytes(B: int, L: int, Hq: int, Hkv: int, D: int = D_SUPPORT
 
 
 def _split_views(ws: torch.Tensor, B: int, Hq: int, nsplit: int, D: int):
+    # workspace layout (include/gqa_attn.h): counters | o_part | lse, 256-byte aligned parts
     rows = B * Hq * nsplit
-    obytes = (rows * D * 4 + 255) // 256 * 256
-    o_part = ws[: rows * D * 4].view(torch.float32).view(B, Hq, nsplit, D)
-    lse = ws[obytes: obytes + rows * 4].view(torch.float32).view(B, Hq, nsplit)
+    o_off = (max(4096, B * Hq) * 4 + 255) // 256 * 256
+    lse_off = o_off + (rows * D * 4 + 255) // 256 * 256
+    o_part = ws[o_off: o_off + rows * D * 4].view(torch.float32).view(B, Hq, nsplit, D)
+    lse = ws[lse_off: lse_off + rows * 4].view(torch.float32).view(B, Hq, nsplit)
     return o_part, lse
 
 
@@ -155,7 +160,7 @@ def decode_partials(q, kcache, vcache, lens, chunk: int, scale: float | None = N
     need = int(lib.gqa_attn_decode_workspace_bytes(B, L, Hq, Hkv, D, int(chunk)))
     if need == 0:
         raise GqaAttnError(_lib.ERR_WORKSPACE, "gqa_attn_decode_workspace_bytes")
-    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws = torch.zeros(need, dtype=torch.uint8, device=q.device)
     rc = lib.gqa_attn_decode_partials(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), lens.data_ptr(),
                                       B, L, Hq, Hkv, D, float(scale), int(chunk), ws.data_ptr(), need,
                                       _stream_ptr(q))

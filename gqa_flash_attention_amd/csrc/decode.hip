@@ -1,229 +1,328 @@
-// decode.hip - one-token GQA decode against a KV cache on gfx950 (kernels K2 and K3).
+// decode.hip - one-token GQA decode against a KV cache on gfx950.
 //
 // Implements the decode mode of the chowfi/kernels README ("Result": generate one token
-// from a KV cache of a given length) with the two decode ideas of its "What helped
-// most" section, redone for CDNA4:
-//  - item 1 (split-KV): the cache is cut into chunks of `chunk` keys; one workgroup per
-//    (chunk, KV head, sequence) spreads a single query over all 256 CUs (K2), and a
-//    second kernel merges the chunks by log-sum-exp (K3);
-//  - item 2 (GQA packing): a K2 workgroup reads each K/V row of its chunk once and
-//    scores it against all query heads of the group (up to 16 per pass) with one
-//    matrix-core instruction.
+// from a KV cache of a given length) with the decode ideas of its "What helped most"
+// section, redone for CDNA4:
+//  - item 1 (split-KV): the cache is cut into chunks; one workgroup per (chunk, KV head,
+//    sequence) spreads a single query over all 256 CUs, and the chunk results are merged
+//    by log-sum-exp;
+//  - item 2 (GQA packing): a workgroup reads each K/V row of its chunk once and scores it
+//    against all query heads of the group (up to 16 per pass) with one matrix-core
+//    instruction;
+//  - item 5 (one fewer launch in short decodes): the merge is fused into the same kernel.
+//    The last workgroup of a (sequence, KV head) to finish merges the partials of all
+//    chunks; with a single chunk the result is written directly.
 //
-// K2 staging: every K/V tile of the chunk (64 rows each) is requested at the start with
-// global_load_lds_dwordx4, so up to 256 rows x 512 B are in flight per workgroup with
-// no register cost, and the chunk's first tiles are computed while later ones arrive.
-// Rows at or past lens[b] are never requested: their addresses are redirected to the
-// last valid row.
+// Streaming. A workgroup walks its chunk in 64-key tiles through an LDS ring of NSTAGE
+// stages (K 16 KB + V 16 KB each). Tiles are copied with global_load_lds_dwordx4 straight
+// from HBM into LDS, NSTAGE-1 tiles ahead, so ~96 KB per CU stay in flight with no
+// register cost. Rows at or past lens[b] are never requested: their addresses are
+// redirected to the last valid row. The library sizes chunks so that a batch-1 decode is
+// about one workgroup per CU, each streaming one contiguous slab of the cache.
 //
-// K2 arithmetic, per wave and 32-key slab: S^T (16 keys x 16 heads, 4 heads real for
-// Llama-3-8B) = K Q^T with v_mfma_f32_16x16x32_bf16 (K from LDS as the A operand, the
-// query heads in registers as B); online softmax in base 2 per head; O^T (d x heads) +=
-// V^T P^T, with V^T read by ds_read_b64_tr_b16 and P^T taken from the score accumulator
-// as is. The waves of the workgroup then merge their (max, sum, O) through LDS, and the
-// workgroup writes the chunk's normalised partial O (fp32) and its log-sum-exp (log2
-// units). Matrix cores keep the arithmetic at a few percent of the HBM time.
+// Arithmetic per wave (16 keys of each tile): S^T (16 keys x 16 heads; 4 heads are real
+// for Llama-3-8B) = K Q^T with v_mfma_f32_16x16x32_bf16, K from LDS as the A operand and
+// the query heads in registers as B; an online softmax in base 2 per head; then
+// O^T (d x heads) += V^T P^T with v_mfma_f32_16x16x16_bf16, whose B operand is the score
+// accumulator layout as is and whose A operand (V^T) comes from ds_read_b64_tr_b16.
+// The four waves merge their (max, sum, O) through LDS at the end of the chunk.
 #include "gqa_device.hpp"
 #include "gqa_internal.hpp"
 
 namespace gqa {
 
-template <int T>
-struct DecodeShape {
-  static constexpr int NW = T == 1 ? 2 : 4;          // waves per workgroup
-  static constexpr int kSlabs = 2 * T;               // 32-key slabs per chunk
-  static constexpr int kLoadsPerTile = 2 * (16 / NW);  // K and V copies per wave per tile
-};
+constexpr int kDecWaves = 4;
+constexpr int kDecLoadsPerTile = 2 * (kTileRows / 4) / kDecWaves;   // K and V copies per wave per tile
 
-template <int T, int N>
-__device__ __forceinline__ void wait_tile() {
-  wait_vmcnt<(T - 1 - N) * DecodeShape<T>::kLoadsPerTile>();
+__device__ __forceinline__ f32x4 mfma16k16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-template <int T>
-__global__ __launch_bounds__(DecodeShape<T>::NW * 64) void decode_split_kernel(DecodeArgs a) {
-  constexpr int NW = DecodeShape<T>::NW;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[T * 2 * kTileBytes];
+// wait until at most `ahead` tiles of this wave's copies are still in flight
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+  switch (ahead) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<kDecLoadsPerTile>(); break;
+    case 2: wait_vmcnt<2 * kDecLoadsPerTile>(); break;
+    default: wait_vmcnt<3 * kDecLoadsPerTile>(); break;
+  }
+}
+
+// Partials cross workgroups (and XCDs, each with its own L2): they are written with
+// device-coherent stores (relaxed atomic stores at agent scope, sc1), which need no
+// write-back of the whole L2 the way a release fence does. The merging workgroup
+// invalidates its own caches once (an acquire fence) and then reads them normally.
+__device__ __forceinline__ void publish(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// FUSE: merge the chunks in the last-arriving workgroup (and write bf16 out); otherwise
+// only write the per-chunk partials.
+template <int NSTAGE, bool FUSE>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+  static_assert(NSTAGE >= 2 && NSTAGE <= 5, "ring depth");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * 2 * kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_q[16 * kRowBytes];
+  __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;      // query head (within the served group) of this lane
+  const int grp = lane >> 4;    // which 4 of the wave's 16 keys this lane scores
   const int split = blockIdx.x;
-  const int g = blockIdx.y / a.hgroups;
-  const int hg = blockIdx.y % a.hgroups;
+  const int gy = blockIdx.y;
+  const int g = gy / a.hgroups;
+  const int hg = gy % a.hgroups;
   const int b = blockIdx.z;
 
   int len = a.lens[b];
   len = len < 0 ? 0 : (len > a.L ? a.L : len);
   const int key_begin = split * a.chunk;
   const int nkeys = min(a.chunk, len - key_begin);
-  const int hbase = 16 * hg;                       // first head (within the group) served
-  const int nheads = min(16, a.G - hbase);         // heads served by this workgroup
-  float* lse_out = a.lse + ((size_t)b * a.Hq + g * a.G + hbase) * a.nsplit + split;
-  if (nkeys <= 0) {
+  const int hbase = 16 * hg;
+  const int nheads = min(16, a.G - hbase);
+  const size_t head0 = (size_t)b * a.Hq + (size_t)g * a.G + hbase;   // first served head row
+  float* lse_out = a.lse + head0 * a.nsplit + split;
+  float* opart = a.o_part + (head0 * a.nsplit + split) * kD;
+
+  if (nkeys > 0) {
+    const int ntiles = (nkeys + kTileRows - 1) / kTileRows;
+    const size_t kv_stride = (size_t)a.Hkv * kD;
+    const size_t row0 = ((size_t)b * a.L + key_begin) * a.Hkv + g;
+    const uint16_t* kbase = a.kc + row0 * kD;
+    const uint16_t* vbase = a.vc + row0 * kD;
+    GQA_LDS uint8_t* const ring = (GQA_LDS uint8_t*)lds;
+
+    // Wave 0 first copies the served query heads (256 B each, 4 heads per instruction);
+    // they are the oldest copies in flight, so the first tile wait covers them.
+    if (wave == 0) {
+      const uint16_t* qrow = a.q + head0 * kD;
+      for (int i = 0; 4 * i < nheads; ++i) {
+        const int hh = min(4 * i + (lane >> 4), nheads - 1);
+        lds_dma16(qrow + (size_t)hh * kD + 8 * (lane & 15), (GQA_LDS uint8_t*)lds_q + i * 1024);
+      }
+    }
+    auto issue = [&](int t) {
+      GQA_LDS uint8_t* st = ring + (t % NSTAGE) * (2 * kTileBytes);
+      const int r0 = t * kTileRows;
+      const size_t off = (size_t)r0 * kv_stride;
+      stage_tile<kDecWaves, false>(st, kbase + off, kv_stride, nkeys - r0, wave, lane);
+      stage_tile<kDecWaves, true>(st + kTileBytes, vbase + off, kv_stride, nkeys - r0, wave, lane);
+    };
+    for (int t = 0; t < NSTAGE - 1; ++t)
+      if (t < ntiles) issue(t);
+
+    const float c = a.c;
+    float m_run = -INFINITY;
+    float l_part = 0.f;
+    f32x4 oacc[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) oacc[mb] = f32x4{};
+    bf16x8 qreg[4];
+
+    for (int t = 0; t < ntiles; ++t) {
+      wait_tiles_ahead(min(NSTAGE - 2, ntiles - 1 - t));
+      // Tile t is in LDS for every wave, and every wave is done with tile t-1, whose
+      // stage the copy below refills.
+      tile_barrier();
+      if (t == 0) {
+        const GQA_LDS uint8_t* qs = (const GQA_LDS uint8_t*)lds_q;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 x = *(const GQA_LDS bf16x8*)(qs + min(n, nheads - 1) * kRowBytes + (4 * ks + grp) * 16);
+          qreg[ks] = n < nheads ? x : bf16x8{};
+        }
+      }
+      if (t + NSTAGE - 1 < ntiles) issue(t + NSTAGE - 1);
+
+      const int kw = t * kTileRows + 16 * wave;   // chunk-relative first key of this wave
+      if (kw < nkeys) {
+        const GQA_LDS uint8_t* kt = ring + (t % NSTAGE) * (2 * kTileBytes);
+        const GQA_LDS uint8_t* vt = kt + kTileBytes;
+        f32x4 s = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          s = mfma16(lds_read_k(kt, 16 * wave + n, 4 * ks + grp), qreg[ks], s);
+        // s[v]: head n, key kw + 4 grp + v
+        float x[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          x[v] = (kw + 4 * grp + v < nkeys) ? s[v] * c : -INFINITY;
+          mx = fmaxf(mx, x[v]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = halves_max(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m_run - m_new);
+        m_run = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) oacc[mb] *= alpha;
+        const __bf16 p0 = (__bf16)exp2_fast(x[0] - m_new), p1 = (__bf16)exp2_fast(x[1] - m_new);
+        const __bf16 p2 = (__bf16)exp2_fast(x[2] - m_new), p3 = (__bf16)exp2_fast(x[3] - m_new);
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0, p1}, one, l_part, false);
+        l_part = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p2, p3}, one, l_part, false);
+        const s16x4 pb = {__builtin_bit_cast(short, p0), __builtin_bit_cast(short, p1),
+                          __builtin_bit_cast(short, p2), __builtin_bit_cast(short, p3)};
+        // A operand V^T for d-block mb: lane holds d = 16mb + n, keys kw + 4grp + 0..3.
+        const int vr = 16 * wave + 4 * grp + (n >> 2);
+        const int vc = 4 * (n & 3);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+          oacc[mb] = mfma16k16(lds_read_v_tr(vt, vr, 16 * mb + vc), pb, oacc[mb]);
+      }
+    }
+
+    // The 4 lane groups of a wave hold disjoint keys of the same heads.
+    l_part += __shfl_xor(l_part, 16);
+    l_part = halves_sum(l_part);
+
+    // Merge the waves through LDS (every copy has landed: the last wait was vmcnt(0)).
+    __syncthreads();
+    GQA_LDS float* wo = (GQA_LDS float*)lds;       // [4][16][128] per-wave O
+    GQA_LDS float* wm = wo + kDecWaves * 16 * kD;  // [4][16] per-wave max
+    GQA_LDS float* wl = wm + kDecWaves * 16;       // [4][16] per-wave sum
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) wo[(wave * 16 + n) * kD + 16 * mb + 4 * grp + v] = oacc[mb][v];
+    if (grp == 0) {
+      wm[wave * 16 + n] = m_run;
+      wl[wave * 16 + n] = l_part;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nheads * kD; idx += 256) {
+      const int hn = idx / kD;
+      const int d = idx % kD;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, wm[w * 16 + hn]);
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float mw = wm[w * 16 + hn];
+        const float sc = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
+        num += sc * wo[(w * 16 + hn) * kD + d];
+        den += sc * wl[w * 16 + hn];
+      }
+      if (FUSE && a.nsplit == 1) {
+        a.out[(head0 + hn) * kD + d] = bf16_bits(num / den);
+      } else {
+        publish(opart + (size_t)hn * a.nsplit * kD + d, num / den);
+        if (d == 0) publish(lse_out + (size_t)hn * a.nsplit, M + log2f(den));
+      }
+    }
+  } else {
     // Nothing to attend in this chunk: weight zero in the merge.
-    if (threadIdx.x < nheads) lse_out[(size_t)threadIdx.x * a.nsplit] = -INFINITY;
-    return;
-  }
-
-  // Wave 0 first copies the served query heads (256 B each, 4 per instruction) into LDS,
-  // then every wave issues its share of all K/V tiles. Every load of the kernel goes
-  // through lds_dma16, so the per-tile waits below account for all of them; wave 0's
-  // query copies are older than its tile copies and are covered by the first wait.
-  const int n = lane & 15;
-  const int grp = lane >> 4;
-  if (wave == 0) {
-    const uint16_t* qrow = a.q + ((size_t)b * a.Hq + g * a.G + hbase) * kD;
-    for (int i = 0; 4 * i < nheads; ++i) {
-      const int hh = min(4 * i + (lane >> 4), nheads - 1);
-      lds_dma16(qrow + (size_t)hh * kD + 8 * (lane & 15), (GQA_LDS uint8_t*)lds_q + i * 1024);
+    if (threadIdx.x < nheads) publish(lse_out + (size_t)threadIdx.x * a.nsplit, -INFINITY);
+    if (FUSE && a.nsplit == 1) {
+      for (int idx = threadIdx.x; idx < nheads * kD; idx += 256) a.out[head0 * kD + idx] = 0;
     }
   }
-  const size_t kv_stride = (size_t)a.Hkv * kD;
-  const size_t row0 = ((size_t)b * a.L + key_begin) * a.Hkv + g;
-  const uint16_t* kbase = a.kc + row0 * kD;
-  const uint16_t* vbase = a.vc + row0 * kD;
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    GQA_LDS uint8_t* kt = (GQA_LDS uint8_t*)lds + (2 * t) * kTileBytes;
-    GQA_LDS uint8_t* vt = (GQA_LDS uint8_t*)lds + (2 * t + 1) * kTileBytes;
-    const int r0 = t * kTileRows;
-    // Rows past the valid keys (tile-relative nvalid <= 0) all map to the chunk's last
-    // valid row, which stays inside the sequence.
-    const int nvalid = nkeys - r0;
-    const size_t off = nvalid > 0 ? (size_t)r0 * kv_stride : (size_t)(nkeys - 1) * kv_stride;
-    stage_tile<NW, false>(kt, kbase + off, kv_stride, nvalid > 0 ? nvalid : 1, wave, lane);
-    stage_tile<NW, true>(vt, vbase + off, kv_stride, nvalid > 0 ? nvalid : 1, wave, lane);
-  }
 
-  const float c = a.c;
-  float m_run = -INFINITY;
-  float l_part = 0.f;
-  f32x4 oacc[8];
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb) oacc[mb] = f32x4{};
+  if (!FUSE || a.nsplit == 1) return;
 
-  bf16x8 qreg[4];
-  auto slab = [&](const GQA_LDS uint8_t* kt, const GQA_LDS uint8_t* vt, int r0, int key0) {
-    // r0: first tile row of the slab; key0: its first key within the chunk.
-    f32x4 s[2] = {f32x4{}, f32x4{}};
+  // Count this chunk. The partial was written with device-coherent stores, and the
+  // barrier below waits for them to complete (vmcnt(0)) before the count, so the
+  // workgroup that counts last sees every chunk's partial. It merges them and resets
+  // the counter for the next call. No workgroup ever waits for another.
+  __syncthreads();
+  int* counter = a.counters + (size_t)b * a.Hkv * a.hgroups + gy;
+  if (threadIdx.x == 0)
+    s_last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.nsplit - 1);
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Drop any stale copy of the partials from this XCD's caches, then read them with
+  // ordinary 16-byte loads.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+  // out[h, d] = sum_s 2^(lse_s - M) o_s[d] / sum_s 2^(lse_s - M), merged with a running
+  // maximum. Thread -> (head, 4 consecutive d) column and a share of the chunks; each
+  // thread fetches kBatch chunks at once so the loads overlap.
+  constexpr int kBatch = 16;
+  const int ncols = nheads * (kD / 4);
+  const int nparts = ncols >= 256 ? 1 : 256 / ncols;
+  GQA_LDS float* red = (GQA_LDS float*)lds;      // [nparts][ncols][6]
+  const float* lse_all = a.lse + head0 * a.nsplit;
+  const float* o_all = a.o_part + head0 * a.nsplit * kD;
+  for (int base = 0; base < ncols * nparts; base += 256) {
+    const int u = base + threadIdx.x;
+    const bool act = u < ncols * nparts;
+    const int col = u % ncols;
+    const int part = u / ncols;
+    const int hn = col / (kD / 4);
+    const int d4 = (col % (kD / 4)) * 4;
+    float m = -INFINITY, den = 0.f;
+    f32x4 num = f32x4{};
+    if (act) {
+      const float* lrow = lse_all + (size_t)hn * a.nsplit;
+      const float* orow = o_all + (size_t)hn * a.nsplit * kD + d4;
+      for (int s0 = part; s0 < a.nsplit; s0 += kBatch * nparts) {
+        float lv[kBatch];
+        f32x4 ov[kBatch];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+        for (int j = 0; j < kBatch; ++j) {
+          const int s = s0 + j * nparts;
+          const bool in = s < a.nsplit;
+          lv[j] = in ? lrow[s] : -INFINITY;
+          ov[j] = in ? *(const f32x4*)(orow + (size_t)s * kD) : f32x4{};
+        }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 kk = lds_read_k(kt, r0 + 16 * blk + n, 4 * ks + grp);
-        s[blk] = mfma16(kk, qreg[ks], s[blk]);
+        for (int j = 0; j < kBatch; ++j) {
+          // An empty chunk (lse = -inf) has no partial: its o_part row is never used.
+          if (lv[j] == -INFINITY) continue;
+          const float mn = fmaxf(m, lv[j]);
+          const float sc_old = (m == -INFINITY) ? 0.f : exp2_fast(m - mn);
+          const float w = exp2_fast(lv[j] - mn);
+          num = num * sc_old + ov[j] * w;
+          den = den * sc_old + w;
+          m = mn;
+        }
       }
     }
-    // s[blk][v]: head n, key key0 + 16 blk + 4 grp + v.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float x = s[blk][v] * c;
-        if (key0 + 16 * blk + 4 * grp + v >= nkeys) x = -INFINITY;
-        s[blk][v] = x;
-        mx = fmaxf(mx, x);
+    if (nparts > 1) {
+      __syncthreads();
+      if (act) {
+        GQA_LDS float* r = red + ((size_t)part * ncols + col) * 6;
+        r[0] = m; r[1] = den; r[2] = num[0]; r[3] = num[1]; r[4] = num[2]; r[5] = num[3];
+      }
+      __syncthreads();
+      if (act && part == 0) {
+        for (int p = 1; p < nparts; ++p) {
+          const GQA_LDS float* r = red + ((size_t)p * ncols + col) * 6;
+          const float mp = r[0];
+          if (mp == -INFINITY) continue;
+          const float mn = fmaxf(m, mp);
+          const float so = (m == -INFINITY) ? 0.f : exp2_fast(m - mn);
+          const float sp = exp2_fast(mp - mn);
+          den = den * so + r[1] * sp;
+          num[0] = num[0] * so + r[2] * sp;
+          num[1] = num[1] * so + r[3] * sp;
+          num[2] = num[2] * so + r[4] * sp;
+          num[3] = num[3] * so + r[5] * sp;
+          m = mn;
+        }
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = halves_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m_run - m_new);
-    m_run = m_new;
-    l_part *= alpha;
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) oacc[mb] *= alpha;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) s[blk][v] = exp2_fast(s[blk][v] - m_new);
-    const bf16x8 p = to_bf16x8(s[0][0], s[0][1], s[0][2], s[0][3], s[1][0], s[1][1], s[1][2], s[1][3]);
-    l_part = sum_bf16x8(p, l_part);
-    // A operand V^T for d-block mb: lane holds d = 16mb + n and keys 4grp+{0..3}, 16+4grp+{0..3}.
-    const int vr = r0 + 4 * grp + (n >> 2);
-    const int vc = 4 * (n & 3);
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const s16x4 lo = lds_read_v_tr(vt, vr, 16 * mb + vc);
-      const s16x4 hi = lds_read_v_tr(vt, vr + 16, 16 * mb + vc);
-      oacc[mb] = mfma16(join_bf16x8(lo, hi), p, oacc[mb]);
+    if (act && part == 0) {
+      typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+      u16x4 w;
+      w[0] = bf16_bits(num[0] * inv);
+      w[1] = bf16_bits(num[1] * inv);
+      w[2] = bf16_bits(num[2] * inv);
+      w[3] = bf16_bits(num[3] * inv);
+      *(u16x4*)(a.out + (head0 + hn) * kD + d4) = w;
     }
-  };
-
-  // Query heads as the B operand (head = lane % 16, d = 32ks + 8(lane/16) + 0..7); heads
-  // past nheads are zero. Read from LDS once the first tile (and so the query) landed.
-  auto load_q = [&]() {
-    const GQA_LDS uint8_t* qs = (const GQA_LDS uint8_t*)lds_q;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 x = *(const GQA_LDS bf16x8*)(qs + min(n, nheads - 1) * kRowBytes + (4 * ks + grp) * 16);
-      qreg[ks] = n < nheads ? x : bf16x8{};
-    }
-  };
-
-  auto tile = [&](auto tn) {
-    constexpr int t = decltype(tn)::value;
-    wait_tile<T, t>();
-    tile_barrier();
-    if (t == 0) load_q();
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      const int sid = 2 * t + sl;
-      if (sid % NW != wave) continue;
-      const int key0 = sid * 32;
-      if (key0 >= nkeys) continue;
-      const GQA_LDS uint8_t* kt = (const GQA_LDS uint8_t*)lds + (2 * t) * kTileBytes;
-      const GQA_LDS uint8_t* vt = (const GQA_LDS uint8_t*)lds + (2 * t + 1) * kTileBytes;
-      slab(kt, vt, 32 * sl, key0);
-    }
-  };
-  tile(std::integral_constant<int, 0>{});
-  if constexpr (T > 1) tile(std::integral_constant<int, 1>{});
-  if constexpr (T > 2) tile(std::integral_constant<int, 2>{});
-  if constexpr (T > 3) tile(std::integral_constant<int, 3>{});
-
-  // The 4 lane groups of a wave hold disjoint keys of the same heads.
-  l_part += __shfl_xor(l_part, 16);
-  l_part = halves_sum(l_part);
-
-  // Merge the waves through LDS (the tiles are no longer needed).
-  __syncthreads();
-  GQA_LDS float* wo = (GQA_LDS float*)lds;       // [NW][16][128] per-wave O
-  GQA_LDS float* wm = wo + NW * 16 * kD;         // [NW][16] per-wave max
-  GQA_LDS float* wl = wm + NW * 16;              // [NW][16] per-wave sum
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) wo[(wave * 16 + n) * kD + 16 * mb + 4 * grp + v] = oacc[mb][v];
-  if (grp == 0) {
-    wm[wave * 16 + n] = m_run;
-    wl[wave * 16 + n] = l_part;
-  }
-  __syncthreads();
-  float* opart = a.o_part + (((size_t)b * a.Hq + g * a.G + hbase) * a.nsplit + split) * kD;
-  for (int idx = threadIdx.x; idx < nheads * kD; idx += NW * 64) {
-    const int hn = idx / kD;
-    const int d = idx % kD;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w * 16 + hn]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = wm[w * 16 + hn];
-      const float sc = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
-      num += sc * wo[(w * 16 + hn) * kD + d];
-      den += sc * wl[w * 16 + hn];
-    }
-    opart[(size_t)hn * a.nsplit * kD + d] = num / den;
-    if (d == 0) lse_out[(size_t)hn * a.nsplit] = M + log2f(den);
   }
 }
 
-// K3: out[b, h, :] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max finite lse_s.
-// Grid (D/32, Hq, B); 256 threads = 8 groups of 32 lanes; lane -> d, group -> splits.
+// Stand-alone merge of per-chunk partials (the second half of a decode on its own):
+// out[b, h, :] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max finite lse_s.
+// Grid (D/32, Hq, B); 256 threads = 8 groups of 32 lanes; lane -> d, group -> chunks.
 __global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs a) {
   __shared__ float red_m[8];
   __shared__ float red_num[8][32];
@@ -248,6 +347,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs a) {
 
   float num = 0.f, den = 0.f;
   if (M != -INFINITY) {
+#pragma unroll 4
     for (int s = grp; s < a.nsplit; s += 8) {
       const float l = lse[s];
       if (l == -INFINITY) continue;
@@ -268,20 +368,24 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs a) {
 }
 
 int decode_default_chunk(int B, int L, int Hkv, int G) {
-  const int hgroups = (G + 15) / 16;
-  const long long wgs128 = (long long)B * Hkv * hgroups * ((L + 127) / 128);
-  return wgs128 < 1024 ? 64 : 128;
+  // About one workgroup per CU for a small batch (each streams one contiguous slab of
+  // the cache), but at least 128 keys per chunk: below that the fixed cost of a
+  // workgroup outweighs the extra parallelism (measured on MI355X for batch 1 and
+  // L = 2K..64K: 128-key chunks are fastest at 2K, ~L/32 from 16K up). A larger batch
+  // keeps chunks at most 1024 keys so ragged sequence lengths still spread evenly.
+  const long long slots = (long long)B * Hkv * ((G + 15) / 16);
+  const long long per = ((long long)L * slots + 255) / 256;
+  long long chunk = (per + kTileRows - 1) / kTileRows * kTileRows;
+  const long long cap = slots >= 64 ? 1024 : 4096;
+  if (chunk < 2 * kTileRows) chunk = 2 * kTileRows;
+  if (chunk > cap) chunk = cap;
+  return (int)chunk;
 }
 
-int launch_decode_split(const DecodeArgs& a, hipStream_t stream) {
+int launch_decode(const DecodeArgs& a, bool fused, hipStream_t stream) {
   const dim3 grid((unsigned)a.nsplit, (unsigned)(a.Hkv * a.hgroups), (unsigned)a.B);
-  switch (a.chunk / kTileRows) {
-    case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(DecodeShape<1>::NW * 64), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(DecodeShape<2>::NW * 64), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(decode_split_kernel<3>, grid, dim3(DecodeShape<3>::NW * 64), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(decode_split_kernel<4>, grid, dim3(DecodeShape<4>::NW * 64), 0, stream, a); break;
-    default: return (int)hipErrorInvalidValue;
-  }
+  if (fused) hipLaunchKernelGGL((decode_kernel<4, true>), grid, dim3(256), 0, stream, a);
+  else       hipLaunchKernelGGL((decode_kernel<4, false>), grid, dim3(256), 0, stream, a);
   return (int)hipGetLastError();
 }
 

@@ -71,21 +71,35 @@ DecodeShapeCheck check_decode_shape(int B, int L, int Hq, int Hkv, int D, float 
   return r;
 }
 
-size_t ws_bytes_for(int B, int Hq, int nsplit) {
+// Workspace layout, each part on a 256-byte boundary:
+//   int32 counters[max(4096, B*Hq)] | fp32 o_part[B][Hq][nsplit][128] | fp32 lse[B][Hq][nsplit].
+// The counters come first and their region depends only on (B, Hq), so a workspace
+// reused for another shape finds its counters where the last call left them: zero.
+// (B*Hq bounds the B*Hkv*ceil(G/16) counters a decode uses.)
+struct WsLayout {
+  size_t o_off, lse_off, cnt_count, total;
+};
+WsLayout ws_layout(int B, int Hq, int nsplit) {
   const size_t rows = (size_t)B * Hq * nsplit;
-  const size_t obytes = (rows * 128 * sizeof(float) + 255) / 256 * 256;
-  return obytes + (rows * sizeof(float) + 255) / 256 * 256;
+  WsLayout w;
+  w.cnt_count = (size_t)B * Hq > 4096 ? (size_t)B * Hq : 4096;
+  w.o_off = (w.cnt_count * sizeof(int) + 255) / 256 * 256;
+  w.lse_off = w.o_off + (rows * 128 * sizeof(float) + 255) / 256 * 256;
+  w.total = w.lse_off + (rows * sizeof(float) + 255) / 256 * 256;
+  return w;
 }
+size_t ws_bytes_for(int B, int Hq, int nsplit) { return ws_layout(B, Hq, nsplit).total; }
 
 // Library-owned decode workspaces, one per (device, stream), grown on demand.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
+  size_t zero_counters = 0;   // leading int32 counters known to be zero
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, void*>, Workspace> g_ws;
 
-int get_workspace(size_t need, hipStream_t stream, void** out) {
+int get_workspace(size_t need, size_t counters, hipStream_t stream, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail("hipGetDevice", e);
@@ -99,12 +113,19 @@ int get_workspace(size_t need, hipStream_t stream, void** out) {
       e = hipFree(w.ptr);
       w.ptr = nullptr;
       w.bytes = 0;
+      w.zero_counters = 0;
       if (e != hipSuccess) return hip_fail("hipFree", e);
     }
     const size_t grow = (need + (1u << 20) - 1) / (1u << 20) * (1u << 20);
     e = hipMalloc(&w.ptr, grow);
     if (e != hipSuccess) { w.ptr = nullptr; return hip_fail("hipMalloc(decode workspace)", e); }
     w.bytes = grow;
+  }
+  if (w.zero_counters < counters) {
+    // The merge counters must start at zero; every completed decode leaves them zero.
+    e = hipMemsetAsync(w.ptr, 0, counters * sizeof(int), stream);
+    if (e != hipSuccess) return hip_fail("hipMemsetAsync(decode counters)", e);
+    w.zero_counters = counters;
   }
   *out = w.ptr;
   return 0;
@@ -118,9 +139,11 @@ gqa::DecodeArgs make_decode_args(const void* q, const void* kc, const void* vc, 
   a.kc = (const uint16_t*)kc;
   a.vc = (const uint16_t*)vc;
   a.lens = lens;
-  const size_t rows = (size_t)B * Hq * s.nsplit;
-  a.o_part = (float*)ws;
-  a.lse = (float*)((char*)ws + (rows * 128 * sizeof(float) + 255) / 256 * 256);
+  const WsLayout w = ws_layout(B, Hq, s.nsplit);
+  a.counters = (int*)ws;
+  a.o_part = (float*)((char*)ws + w.o_off);
+  a.lse = (float*)((char*)ws + w.lse_off);
+  a.out = nullptr;
   a.B = B; a.L = L; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
   a.hgroups = s.hgroups;
   a.chunk = s.chunk;
@@ -133,11 +156,9 @@ int run_decode(const void* q, const void* kc, const void* vc, const int32_t* len
                int B, int L, int Hq, int Hkv, float scale, const DecodeShapeCheck& s,
                void* ws, hipStream_t stream) {
   gqa::DecodeArgs a = make_decode_args(q, kc, vc, lens, B, L, Hq, Hkv, scale, s, ws);
-  int e = gqa::launch_decode_split(a, stream);
-  if (e != 0) return hip_fail("decode split launch", e);
-  gqa::CombineArgs cmb{a.o_part, a.lse, (uint16_t*)out, B, Hq, s.nsplit};
-  e = gqa::launch_decode_combine(cmb, stream);
-  if (e != 0) return hip_fail("decode combine launch", e);
+  a.out = (uint16_t*)out;
+  int e = gqa::launch_decode(a, true, stream);
+  if (e != 0) return hip_fail("decode launch", e);
   return GQA_ATTN_OK;
 }
 
@@ -154,7 +175,7 @@ const char* gqa_attn_strerror(int code) {
     case GQA_ATTN_ERR_DIM: return "bad dimension or scale (sizes < 1, Hq % Hkv != 0, non-finite scale, or sizes too large)";
     case GQA_ATTN_ERR_UNSUPPORTED: return "unsupported: head dim must be 128 and pointers 16-byte aligned";
     case GQA_ATTN_ERR_HIP: return "HIP launch or allocation failure";
-    case GQA_ATTN_ERR_WORKSPACE: return "workspace missing or too small, or split size not a multiple of 64 in [64, 256]";
+    case GQA_ATTN_ERR_WORKSPACE: return "workspace missing or too small, or split size not a positive multiple of 64";
     default: return "unknown error code";
   }
 }
@@ -213,7 +234,8 @@ int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
   if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out))
     return GQA_ATTN_ERR_UNSUPPORTED;
   void* ws = nullptr;
-  int e = get_workspace(ws_bytes_for(B, Hq, s.nsplit), (hipStream_t)stream, &ws);
+  const WsLayout w = ws_layout(B, Hq, s.nsplit);
+  int e = get_workspace(w.total, w.cnt_count, (hipStream_t)stream, &ws);
   if (e) return e;
   return run_decode(q, kcache, vcache, lens, out, B, L, Hq, Hkv, scale, s, ws, (hipStream_t)stream);
 }
@@ -240,8 +262,8 @@ int gqa_attn_decode_partials(const void* q, const void* kcache, const void* vcac
   if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache)) return GQA_ATTN_ERR_UNSUPPORTED;
   if (!ws || !aligned16(ws) || ws_bytes < ws_bytes_for(B, Hq, s.nsplit)) return GQA_ATTN_ERR_WORKSPACE;
   gqa::DecodeArgs a = make_decode_args(q, kcache, vcache, lens, B, L, Hq, Hkv, scale, s, ws);
-  int e = gqa::launch_decode_split(a, (hipStream_t)stream);
-  if (e != 0) return hip_fail("decode split launch", e);
+  int e = gqa::launch_decode(a, false, (hipStream_t)stream);
+  if (e != 0) return hip_fail("decode partials launch", e);
   return GQA_ATTN_OK;
 }
 
@@ -252,11 +274,10 @@ int gqa_attn_decode_combine(const void* ws, size_t ws_bytes, void* out,
   if (D != 128) return GQA_ATTN_ERR_UNSUPPORTED;
   if (elems4(B, Hq, nsplit) < 0 || B > kMaxGridY || Hq > kMaxGridY) return GQA_ATTN_ERR_DIM;
   if (!aligned16(ws) || !aligned16(out)) return GQA_ATTN_ERR_UNSUPPORTED;
-  if (ws_bytes < ws_bytes_for(B, Hq, nsplit)) return GQA_ATTN_ERR_WORKSPACE;
-  const size_t rows = (size_t)B * Hq * nsplit;
-  gqa::CombineArgs cmb{(const float*)ws,
-                       (const float*)((const char*)ws + (rows * 128 * sizeof(float) + 255) / 256 * 256),
-                       (uint16_t*)out, B, Hq, nsplit};
+  const WsLayout w = ws_layout(B, Hq, nsplit);
+  if (ws_bytes < w.total) return GQA_ATTN_ERR_WORKSPACE;
+  gqa::CombineArgs cmb{(const float*)((const char*)ws + w.o_off),
+                       (const float*)((const char*)ws + w.lse_off), (uint16_t*)out, B, Hq, nsplit};
   int e = gqa::launch_decode_combine(cmb, (hipStream_t)stream);
   if (e != 0) return hip_fail("decode combine launch", e);
   return GQA_ATTN_OK;

@@ -26,6 +26,8 @@ struct DecodeArgs {
   const int32_t* lens;   // [B], device
   float* o_part;         // [B, Hq, nsplit, D]
   float* lse;            // [B, Hq, nsplit], log2 units
+  int* counters;         // [B, Hkv * hgroups] arrival counters of the fused merge (zero between calls)
+  uint16_t* out;         // [B, Hq, D] (fused kernel only)
   int B, L, Hq, Hkv, G;
   int hgroups;           // ceil(G / 16): query heads are served 16 at a time
   int chunk;             // keys per split, a multiple of 64
@@ -42,12 +44,14 @@ struct CombineArgs {
 
 // Each returns a hipError_t value (0 = success) from the launch.
 int launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
-int launch_decode_split(const DecodeArgs& a, hipStream_t stream);
+// fused = true: split, then merge in the last-arriving workgroup, writing `out`.
+// fused = false: only the per-chunk partials (o_part, lse).
+int launch_decode(const DecodeArgs& a, bool fused, hipStream_t stream);
 int launch_decode_combine(const CombineArgs& a, hipStream_t stream);
 
 // Keys per split chosen for a decode of this shape (a multiple of 64).
 int decode_default_chunk(int B, int L, int Hkv, int G);
-// Largest supported keys per split.
-constexpr int kMaxChunk = 256;
+// Largest accepted keys per split.
+constexpr int kMaxChunk = 1 << 24;
 
 }  // namespace gqa

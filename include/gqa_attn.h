@@ -76,13 +76,14 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, void* out,
  *                    or past lens[b] are never read, whatever they hold.
  * Implements the decode mode ("Result": decode generates one token from a KV
  * cache of a given length). The cache is cut into chunks that run in parallel
- * on all CUs and are then merged by a log-sum-exp combine ("What helped most",
- * item 1). Each chunk's K/V rows are read once for all query heads of their
- * group (item 2).
- * The split partials live in a library-owned workspace, cached per device and
- * grown on demand (one hipMalloc the first time a larger size is needed on a
- * device; none afterwards). The workspace is not shared across streams: each
- * (device, stream) pair gets its own, so concurrent streams never race.
+ * on all CUs and are then merged by log-sum-exp ("What helped most", item 1).
+ * Each chunk's K/V rows are read once for all query heads of their group
+ * (item 2). The merge happens in the same kernel launch (item 5, one fewer
+ * launch): the last workgroup to finish a (sequence, KV head) merges it.
+ * The split partials live in a library-owned workspace, cached per (device,
+ * stream) and grown on demand: one hipMalloc (and a clear of the new buffer)
+ * the first time a larger size is needed, none afterwards. Concurrent streams
+ * never share a workspace.
  */
 int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
                     const int32_t* lens, void* out,
@@ -99,7 +100,10 @@ int gqa_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int* chunk, int* 
 /*
  * Bytes of workspace a decode needs with `chunk` keys per split (0 = the
  * library's own choice). Returns 0 if the arguments are invalid.
- * Layout: fp32 o_part[B][Hq][nsplit][D], then fp32 lse[B][Hq][nsplit].
+ * Layout, each part on a 256-byte boundary: int32 counters[max(4096, B*Hq)],
+ * then fp32 o_part[B][Hq][nsplit][D], then fp32 lse[B][Hq][nsplit]. The
+ * counters come first and their size depends only on (B, Hq), so a zeroed
+ * workspace stays valid when it is reused for other shapes.
  */
 size_t gqa_attn_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int D, int chunk);
 
@@ -108,6 +112,9 @@ size_t gqa_attn_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int D, int
  * semantics as gqa_attn_decode. chunk = 0 takes the library's choice;
  * otherwise chunk must be a positive multiple of 64. ws must be 16-byte
  * aligned and hold at least gqa_attn_decode_workspace_bytes(..., chunk) bytes.
+ * The counters part of ws (its first max(4096, B*Hq) int32) must hold zeros
+ * before the call: allocate the buffer zeroed; each completed call leaves the
+ * counters zero again. Two calls in flight on the same workspace race.
  * Allocates nothing.
  */
 int gqa_attn_decode_ws(const void* q, const void* kcache, const void* vcache,
@@ -123,7 +130,8 @@ int gqa_attn_decode_ws(const void* q, const void* kcache, const void* vcache,
  *                       i.e. the chunk's log-sum-exp in base-2 units;
  *                       -inf for an empty chunk; such a chunk's o_part row is not
  *                       written and must be ignored).
- * ws is laid out as in gqa_attn_decode_workspace_bytes. Allocates nothing.
+ * ws is laid out as in gqa_attn_decode_workspace_bytes (the counters are not
+ * used). Allocates nothing.
  */
 int gqa_attn_decode_partials(const void* q, const void* kcache, const void* vcache,
                              const int32_t* lens, int B, int L, int Hq, int Hkv, int D,
@@ -131,8 +139,8 @@ int gqa_attn_decode_partials(const void* q, const void* kcache, const void* vcac
 
 /*
  * The second half of a decode on its own: log-sum-exp merge of nsplit
- * partials (laid out as above) into out [B, Hq, D] bf16. A row whose every
- * split is empty becomes zero. Allocates nothing.
+ * partials (o_part then lse, laid out as above) into out [B, Hq, D] bf16.
+ * A row whose every split is empty becomes zero. Allocates nothing.
  */
 int gqa_attn_decode_combine(const void* ws, size_t ws_bytes, void* out,
                             int B, int Hq, int D, int nsplit, void* stream);

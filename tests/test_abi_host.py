@@ -101,7 +101,7 @@ def test_decode_ws_and_split_errors(lib):
     assert call(ws=None) == _lib.ERR_WORKSPACE
     assert call(ws=MIS) == _lib.ERR_WORKSPACE
     assert call(ws_bytes=need - 1) == _lib.ERR_WORKSPACE
-    for bad in (1, 63, 100, 320, -64):
+    for bad in (1, 63, 100, 96, -64):
         assert call(chunk=bad) == _lib.ERR_WORKSPACE, bad
     assert lib.gqa_attn_decode_workspace_bytes(1, 1000, 32, 8, 128, 100) == 0
     rc = lib.gqa_attn_decode_partials(P, P, P, P, 1, 1000, 32, 8, 128, 0.088, 128, P, need - 1, None)
@@ -118,11 +118,17 @@ def test_decode_plan_and_workspace_size(lib):
     nsplit = ctypes.c_int(0)
     for L in (1, 63, 64, 2048, 16384, 65536, 50001):
         assert lib.gqa_attn_decode_plan(1, L, 32, 8, 128, ctypes.byref(chunk), ctypes.byref(nsplit)) == 0
-        assert chunk.value % 64 == 0 and 64 <= chunk.value <= 256
+        assert chunk.value % 64 == 0 and 64 <= chunk.value <= 4096
         assert nsplit.value == -(-L // chunk.value)
         ws = lib.gqa_attn_decode_workspace_bytes(1, L, 32, 8, 128, 0)
         rows = 32 * nsplit.value
-        assert ws == (rows * 128 * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
+        counters = max(4096, 32)
+        assert ws == ((counters * 4 + 255) // 256 * 256 + (rows * 128 * 4 + 255) // 256 * 256
+                      + (rows * 4 + 255) // 256 * 256)
+    # batch-1 decodes of the workload are cut into about one chunk per CU (256 CUs)
+    for L in (16384, 32768, 65536):
+        assert lib.gqa_attn_decode_plan(1, L, 32, 8, 128, ctypes.byref(chunk), ctypes.byref(nsplit)) == 0
+        assert nsplit.value * 8 == 256, (L, chunk.value, nsplit.value)
     assert lib.gqa_attn_decode_plan(1, 100, 32, 8, 128, None, None) == 0
     assert lib.gqa_attn_decode_plan(0, 100, 32, 8, 128, None, None) == _lib.ERR_DIM
 

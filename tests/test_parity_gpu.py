@@ -181,7 +181,8 @@ def test_decode_ragged_batch_nan_poisoned():
 
 
 @pytest.mark.parametrize("L,chunk", [(256, 256), (128, 64), (192, 64), (400, 64), (1000, 128),
-                                     (1000, 192), (5000, 256), (64, 64), (65, 64)])
+                                     (1000, 192), (5000, 256), (64, 64), (65, 64), (3000, 512),
+                                     (3000, 3008), (5000, 1024), (20000, 4096), (777, 832)])
 def test_decode_forced_splits(L, chunk):
     nsplit = -(-L // chunk)
     _say(f"decode B=2 L={L} chunk={chunk} (nsplit={nsplit}), ragged lens, NaN padding")
@@ -197,10 +198,10 @@ def test_decode_split_counts_agree():
     q, kc, vc, lens = decode_inputs(1, L, base=8100)
     want = oracle.decode(bf16_bits(q), bf16_bits(kc), bf16_bits(vc), lens)
     outs = {}
-    for chunk in (64, 128, 192, 256):
+    for chunk in (64, 128, 192, 256, 640, 1024, 3008):
         outs[chunk] = gpu_f64(_decode_gpu(q, kc, vc, lens, chunk=chunk))
         assert_close(outs[chunk], want, f"chunk={chunk}")
-    for c in (128, 192, 256):
+    for c in (128, 192, 256, 640, 1024, 3008):
         assert np.max(np.abs(outs[c] - outs[64])) <= 2e-2
 
 
@@ -237,6 +238,30 @@ def test_decode_single_key_exact_and_empty_and_clamped():
     assert torch.all(out[1].float() == 0) and torch.all(out[3].float() == 0)
     want = oracle.decode(bf16_bits(q), bf16_bits(kc), bf16_bits(vc), [1, 0, L, 0])
     assert_close(gpu_f64(out), want, "decode lens edge cases")
+
+
+def test_decode_single_split_with_empty_sequence():
+    _say("decode B=3 L=500 one split (chunk 512), lens = [500, 0, 37]")
+    q, kc, vc, lens = decode_inputs(3, 500, base=8350, lens=[500, 0, 37], poison=True)
+    out = _decode_gpu(q, kc, vc, lens, chunk=512)
+    assert torch.all(out[1].float().cpu() == 0)
+    want = oracle.decode(bf16_bits(q), bf16_bits(kc), bf16_bits(vc), lens)
+    assert_close(gpu_f64(out), want, "decode one split")
+
+
+def test_decode_workspace_reused_across_calls():
+    _say("decode with one caller workspace, two calls in a row (second smaller): merge counters reset")
+    q, kc, vc, lens = decode_inputs(2, 4000, base=8360, lens=[4000, 2500], poison=True)
+    need = gqa.decode_workspace_bytes(2, 4000, HQ, HKV, D, 256)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    out1 = gqa.decode(dev(q), dev(kc), dev(vc), dev(lens), chunk=256, workspace=ws)
+    q2, kc2, vc2, lens2 = decode_inputs(1, 1500, base=8361, lens=[1400], poison=True)
+    out2 = gqa.decode(dev(q2), dev(kc2), dev(vc2), dev(lens2), chunk=256, workspace=ws)
+    out3 = gqa.decode(dev(q), dev(kc), dev(vc), dev(lens), chunk=256, workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(gpu_f64(out1), oracle.decode(bf16_bits(q), bf16_bits(kc), bf16_bits(vc), lens), "call 1")
+    assert_close(gpu_f64(out2), oracle.decode(bf16_bits(q2), bf16_bits(kc2), bf16_bits(vc2), lens2), "call 2")
+    assert torch.equal(out1.cpu(), out3.cpu())
 
 
 def test_decode_other_group_sizes_and_scales():
