@@ -102,12 +102,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         lds_dma16(qrow + (size_t)hh * kD + 8 * (lane & 15), (GQA_LDS uint8_t*)lds_q + i * 1024);
       }
     }
+    TileCopy<kDecWaves> copy;
+    copy.init(kv_stride, wave, lane);
+    // Copies of tile t (K then V): per-lane offsets for a full tile, the clamped per-row
+    // path for the ragged last tile.
     auto issue = [&](int t) {
       GQA_LDS uint8_t* st = ring + (t % NSTAGE) * (2 * kTileBytes);
       const int r0 = t * kTileRows;
       const size_t off = (size_t)r0 * kv_stride;
-      stage_tile<kDecWaves, false>(st, kbase + off, kv_stride, nkeys - r0, wave, lane);
-      stage_tile<kDecWaves, true>(st + kTileBytes, vbase + off, kv_stride, nkeys - r0, wave, lane);
+      if (nkeys - r0 >= kTileRows) {
+        copy.issue_full(st, st + kTileBytes, kbase + off, vbase + off, wave);
+      } else {
+        stage_tile<kDecWaves, false>(st, kbase + off, kv_stride, nkeys - r0, wave, lane);
+        stage_tile<kDecWaves, true>(st + kTileBytes, vbase + off, kv_stride, nkeys - r0, wave, lane);
+      }
     };
     for (int t = 0; t < NSTAGE - 1; ++t)
       if (t < ntiles) issue(t);

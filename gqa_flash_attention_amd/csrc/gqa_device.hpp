@@ -63,13 +63,45 @@ __device__ __forceinline__ int swz_v(int r) { return ((r & 1) ? 6 : 0) ^ ((r & 2
 // tile. Vector-memory loads complete in issue order, so the waits the compiler derives
 // for its own loads stay conservative; the tile pipelines wait for these copies
 // themselves (wait_vmcnt) before the barrier that publishes a tile.
+// The LDS address travels in M0, passed as an operand so the compiler sets (and owns)
+// M0; the leading s_nop covers the M0-write hazard before the copy reads it.
 __device__ __forceinline__ void lds_dma16(const void* gptr, GQA_LDS void* lds) {
   const uint32_t m0 = (uint32_t)(uintptr_t)lds;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(m0)
-               : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "{m0}"(m0) : "memory");
 }
+
+// Same copy with the global address split into a wave-uniform 64-bit base (SGPRs) and a
+// 32-bit per-lane byte offset (the saddr form): no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, GQA_LDS void* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)lds;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+
+// Per-lane byte offsets of a full 64-row K tile and V tile, computed once per kernel:
+// the copy of any full tile is then just (tile base, offset) per instruction.
+template <int NW>
+struct TileCopy {
+  static constexpr int kPer = (kTileRows / 4) / NW;   // instructions per wave per tile
+  uint32_t ko[kPer], vo[kPer];
+  __device__ __forceinline__ void init(size_t row_stride_elems, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int r = 4 * (wave + NW * j) + (lane >> 4);
+      const int slot = lane & 15;
+      const uint32_t row = (uint32_t)(r * row_stride_elems * 2);
+      ko[j] = row + (uint32_t)((slot ^ swz_k(r)) << 4);
+      vo[j] = row + (uint32_t)((slot ^ swz_v(r)) << 4);
+    }
+  }
+  // All 64 rows valid: K then V, kPer copies each for this wave.
+  __device__ __forceinline__ void issue_full(GQA_LDS uint8_t* kt, GQA_LDS uint8_t* vt,
+                                             const uint16_t* kg, const uint16_t* vg, int wave) const {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) lds_dma16_sv(kg, ko[j], kt + (wave + NW * j) * 1024);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) lds_dma16_sv(vg, vo[j], vt + (wave + NW * j) * 1024);
+  }
+};
 
 // Issue the HBM->LDS copies of one 64-row tile. `rows` points at row 0 of the tile's
 // head in global memory; consecutive rows are `row_stride` bf16 apart. Rows at or past

@@ -77,9 +77,22 @@ void prefill_kernel(PrefillArgs a) {
   const uint16_t* kbase = a.k + ((size_t)b * a.S * a.Hkv + g) * kD;
   const uint16_t* vbase = a.v + ((size_t)b * a.S * a.Hkv + g) * kD;
 
+  TileCopy<4> copy;
+  copy.init(kv_stride, wave, lane);
+  // Copies of tile t (K then V): the per-lane offsets for a full tile, the clamped
+  // per-row path for the ragged last tile.
+  auto issue_tile = [&](int t, GQA_LDS uint8_t* kd, GQA_LDS uint8_t* vd) {
+    const int r0 = t * kTileRows;
+    if (kv_end - r0 >= kTileRows) {
+      copy.issue_full(kd, vd, kbase + (size_t)r0 * kv_stride, vbase + (size_t)r0 * kv_stride, wave);
+    } else {
+      stage_tile<4, false>(kd, kbase + (size_t)r0 * kv_stride, kv_stride, kv_end - r0, wave, lane);
+      stage_tile<4, true>(vd, vbase + (size_t)r0 * kv_stride, kv_stride, kv_end - r0, wave, lane);
+    }
+  };
+
   // Prologue: start tile 0, then fetch this wave's Q rows (B operand, 8 k-steps of 16 d).
-  stage_tile<4, false>(K0, kbase, kv_stride, kv_end, wave, lane);
-  stage_tile<4, true>(V0, vbase, kv_stride, kv_end, wave, lane);
+  issue_tile(0, K0, V0);
   bf16x8 qreg[8];
   {
     const int qrow = min(q0 + qi, a.S - 1);
@@ -111,9 +124,7 @@ void prefill_kernel(PrefillArgs a) {
     // its LDS reads of them fed MFMAs that have issued, so they have completed.
     tile_barrier();
     if (t + 1 < nt) {
-      const int r0 = (t + 1) * kTileRows;
-      stage_tile<4, false>(kn, kbase + (size_t)r0 * kv_stride, kv_stride, kv_end - r0, wave, lane);
-      stage_tile<4, true>(vn, vbase + (size_t)r0 * kv_stride, kv_stride, kv_end - r0, wave, lane);
+      issue_tile(t + 1, kn, vn);
       wait_vmcnt<8>();   // this wave's copies of tile t have landed (8 of t+1 may remain)
     } else {
       wait_vmcnt<0>();
@@ -121,14 +132,23 @@ void prefill_kernel(PrefillArgs a) {
     tile_barrier();      // ... and so have every other wave's
     if (!active || t >= own_nt) return;
 
-    // S^T[key][query] for the tile's 64 keys, two 32-key blocks.
+    // S^T[key][query] for the tile's 64 keys, two 32-key blocks. The K operand reads run
+    // 4 k-steps ahead of the MFMAs that consume them.
     f32x16 s0 = f32x16{}, s1 = f32x16{};
+    bf16x8 ka[4], kb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      ka[ks] = lds_read_k(kt, qi, 2 * ks + h);
+      kb[ks] = lds_read_k(kt, 32 + qi, 2 * ks + h);
+    }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 a0 = lds_read_k(kt, qi, 2 * ks + h);
-      const bf16x8 a1 = lds_read_k(kt, 32 + qi, 2 * ks + h);
-      s0 = mfma32(a0, qreg[ks], s0);
-      s1 = mfma32(a1, qreg[ks], s1);
+      s0 = mfma32(ka[ks & 3], qreg[ks], s0);
+      s1 = mfma32(kb[ks & 3], qreg[ks], s1);
+      if (ks + 4 < 8) {
+        ka[ks & 3] = lds_read_k(kt, qi, 2 * (ks + 4) + h);
+        kb[ks & 3] = lds_read_k(kt, 32 + qi, 2 * (ks + 4) + h);
+      }
     }
     if (!POS) {
 #pragma unroll
@@ -163,34 +183,45 @@ void prefill_kernel(PrefillArgs a) {
       m_run = m_new;
     }
     const float neg_m = -m_run;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      s0[v] = exp2_fast(POS ? __builtin_fmaf(s0[v], c, neg_m) : s0[v] + neg_m);
-      s1[v] = exp2_fast(POS ? __builtin_fmaf(s1[v], c, neg_m) : s1[v] + neg_m);
-    }
-    // P^T as the B operand of O^T = V^T P^T: 4 k-steps of 16 keys, straight from the
-    // accumulator layout (k index 8h+u <-> key 16t4 + 8(u/4) + 4h + u%4).
-    bf16x8 p[4];
-    p[0] = to_bf16x8(s0[0], s0[1], s0[2], s0[3], s0[4], s0[5], s0[6], s0[7]);
-    p[1] = to_bf16x8(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
-    p[2] = to_bf16x8(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
-    p[3] = to_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) l_part = sum_bf16x8(p[t4], l_part);
-
-    // O^T[d][query] += V^T[d][key] P^T[key][query]. The A operand for d-block mb and
-    // k-step t4: lane l holds d = 32mb + l%32 and keys 16t4 + 4(l/32) + {0..3, 8..11}.
+    // O^T[d][query] += V^T[d][key] P^T[key][query], 4 k-steps of 16 keys. P^T is the B
+    // operand straight from the accumulator layout (k index 8h+u <-> key
+    // 16t4 + 8(u/4) + 4h + u%4). For d-block mb the A operand has lane l holding
+    // d = 32mb + l%32 and keys 16t4 + 4(l/32) + {0..3, 8..11}, read transposed from LDS.
+    // Each step's probabilities are formed just before its MFMAs and the next step's V
+    // reads are already in flight, so exp work overlaps the matrix cores.
     const int g16 = lane >> 4;
     const int li = lane & 15;
     const int vrow = 4 * (g16 >> 1) + (li >> 2);
     const int vcol = 16 * (g16 & 1) + 4 * (li & 3);
+    s16x4 vlo[4], vhi[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      vlo[mb] = lds_read_v_tr(vt, vrow, 32 * mb + vcol);
+      vhi[mb] = lds_read_v_tr(vt, 8 + vrow, 32 * mb + vcol);
+    }
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
+      const f32x16& sb = (t4 < 2) ? s0 : s1;
+      const int o = 8 * (t4 & 1);
+      float e[8];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const s16x4 lo = lds_read_v_tr(vt, 16 * t4 + vrow, 32 * mb + vcol);
-        const s16x4 hi = lds_read_v_tr(vt, 16 * t4 + 8 + vrow, 32 * mb + vcol);
-        oacc[mb] = mfma32(join_bf16x8(lo, hi), p[t4], oacc[mb]);
+      for (int u = 0; u < 8; ++u)
+        e[u] = exp2_fast(POS ? __builtin_fmaf(sb[o + u], c, neg_m) : sb[o + u] + neg_m);
+      const bf16x8 p = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      l_part = sum_bf16x8(p, l_part);
+      s16x4 nlo[4], nhi[4];
+      if (t4 < 3) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          nlo[mb] = lds_read_v_tr(vt, 16 * (t4 + 1) + vrow, 32 * mb + vcol);
+          nhi[mb] = lds_read_v_tr(vt, 16 * (t4 + 1) + 8 + vrow, 32 * mb + vcol);
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) oacc[mb] = mfma32(join_bf16x8(vlo[mb], vhi[mb]), p, oacc[mb]);
+      if (t4 < 3) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) { vlo[mb] = nlo[mb]; vhi[mb] = nhi[mb]; }
       }
     }
   };
