@@ -44,6 +44,11 @@ def prefill_flops(S: int, B: int = 1) -> float:
     return 2.0 * 2.0 * S * (S + 1) / 2.0 * HQ * D * B
 
 
+def prefill_bytes(S: int, B: int = 1) -> float:
+    """q, k, v read once and out written once."""
+    return float(S * B * (HQ + HKV + HKV + HQ) * D * 2)
+
+
 def decode_bytes(L_total: int, B: int = 1) -> float:
     """K+V read once per KV head for L_total cached tokens, plus q and out."""
     return 2.0 * L_total * HKV * D * 2 + 2.0 * B * HQ * D * 2
@@ -158,6 +163,18 @@ def run_step_timing(S, L, steps, warmup):
     return wall, pf, dc
 
 
+def calibration_copy(mib: int) -> None:
+    """One plain device-to-device copy of a known size, run outside the timed region so a
+    counter pass over this process can scale FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def main_line(args):
     import torch
     S, L = args.prefill_s, args.decode_l
@@ -210,6 +227,8 @@ def main_line(args):
     }
     if args.cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(S, budget_s=args.cpu_budget)
+    if args.calib_copy_mb:
+        calibration_copy(args.calib_copy_mb)
     print(json.dumps(line), flush=True)
 
 
@@ -273,12 +292,14 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--prefill-s", type=int, default=32768)
     ap.add_argument("--decode-l", type=int, default=65536)
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU baseline")
     ap.add_argument("--sweep", metavar="OUT_JSONL", default=None)
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after the timed steps, one device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "

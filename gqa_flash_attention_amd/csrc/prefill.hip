@@ -133,7 +133,10 @@ void prefill_kernel(PrefillArgs a) {
     if (!active || t >= own_nt) return;
 
     // S^T[key][query] for the tile's 64 keys, two 32-key blocks. The K operand reads run
-    // 4 k-steps ahead of the MFMAs that consume them.
+    // 4 k-steps ahead of the MFMAs that consume them. The wave raises its issue priority
+    // while it feeds the matrix cores, so that on a SIMD shared with a wave doing softmax
+    // work the MFMA stream is not starved.
+    __builtin_amdgcn_s_setprio(1);
     f32x16 s0 = f32x16{}, s1 = f32x16{};
     bf16x8 ka[4], kb[4];
 #pragma unroll
@@ -150,6 +153,7 @@ void prefill_kernel(PrefillArgs a) {
         kb[ks & 3] = lds_read_k(kt, 32 + qi, 2 * (ks + 4) + h);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (!POS) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) { s0[v] *= c; s1[v] *= c; }
@@ -194,6 +198,7 @@ void prefill_kernel(PrefillArgs a) {
     const int vrow = 4 * (g16 >> 1) + (li >> 2);
     const int vcol = 16 * (g16 & 1) + 4 * (li & 3);
     s16x4 vlo[4], vhi[4];
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       vlo[mb] = lds_read_v_tr(vt, vrow, 32 * mb + vcol);
@@ -224,6 +229,7 @@ void prefill_kernel(PrefillArgs a) {
         for (int mb = 0; mb < 4; ++mb) { vlo[mb] = nlo[mb]; vhi[mb] = nhi[mb]; }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   for (int t = 0; t < nt; t += 2) {
