@@ -28,7 +28,7 @@ HQ, HKV, D = 32, 8, 128
 BF16_NAN_BITS = 0x7FC0   # a quiet bf16 NaN, used to poison unused cache slots
 
 __all__ = [
-    "HQ", "HKV", "D", "BF16_NAN_BITS", "seed_base", "randn_bf16",
+    "HQ", "HKV", "D", "BF16_NAN_BITS", "seed_base", "randn_bf16", "randn_bf16_device",
     "prefill_inputs", "decode_inputs", "random_lens", "bf16_bits",
 ]
 
@@ -43,6 +43,17 @@ def randn_bf16(shape, seed: int, sigma: float = 1.0) -> torch.Tensor:
     x = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
     if sigma != 1.0:
         x = x * float(sigma)
+    return x.to(torch.bfloat16)
+
+
+def randn_bf16_device(shape, seed: int, device, sigma: float = 1.0) -> torch.Tensor:
+    """bf16 N(0, sigma^2) values drawn on the device from ``seed`` (for inputs too large to
+    draw on the host). The same seed and device give the same bits; copy a slice to the
+    host to hand it to a CPU reference."""
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=device)
+    if sigma != 1.0:
+        x.mul_(float(sigma))
     return x.to(torch.bfloat16)
 
 
