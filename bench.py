@@ -221,7 +221,7 @@ def main_line(args):
             "bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
             "traffic": load_traffic(f"decode_L{L}"),
-            "kernel": "decode_split_kernel + decode_combine_kernel",
+            "kernel": "decode_kernel<fused> (split-KV + in-kernel merge, one launch)",
         },
         "device": torch.cuda.get_device_name(0),
     }
