@@ -11,13 +11,16 @@ Printed (rank 0, one JSON line): the contract fields, with
 - value      : causal prefill TFLOP/s (FLOPs = 2*2*S*(S+1)/2*Hq*D, the causal half);
 - decode     : decode KV-read GB/s (bytes = K+V read once = 2*L*Hkv*D*2, plus q and out);
 - roofline   : the prefill kernel against the bf16 dense MFMA peak (it is most of the step);
-- roofline_decode : the decode kernels against the HBM peak;
+- roofline_decode : the decode kernel against the HBM peak;
+  both also carry measured_peak / frac_of_measured: the same kernel against the rate
+  the library's own probes reach on this board (cold 16-byte HBM reads; register-resident
+  bf16 MFMA with random operands, with the clock it ran at), taken after the timed steps;
 - cpu_baseline: the fp64 CPU oracle on a bounded sample of the same prefill.
 Kernel durations come from HIP events recorded on the stream the kernels run on,
 inside the timed region. The prefill streams ~671 MB between decodes, which flushes
 the 256 MB MALL, so every decode reads its cache from HBM.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-probes]
     python bench.py --sweep out.jsonl     # every prefill/decode size, one JSON line each
 """
 
@@ -163,6 +166,55 @@ def run_step_timing(S, L, steps, warmup):
     return wall, pf, dc
 
 
+def measured_roofs():
+    """Run the library's two roofline probes (gqa_attn_probe_*): the cold HBM read rate
+    over a 2 GiB buffer (8x the MALL) and the register-resident bf16 MFMA rate with random
+    operands, with the shader clock it ran at. Each is the median of 3 timed calls after
+    one warm-up call, events on torch's current stream."""
+    import torch
+    from gqa_flash_attention_amd import _lib
+    lib = _lib.get()
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    out = {}
+
+    def timed(fn, n=3):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    wg = 4096
+    sink = torch.empty(wg * 256, dtype=torch.int32, device=dev)
+    ms = timed(lambda: _lib.check(lib.gqa_attn_probe_hbm_read(buf.data_ptr(), nbytes, wg, sink.data_ptr(),
+                                                             sink.numel(), st.cuda_stream), "probe_hbm_read"))
+    out["hbm"] = {"value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                  "method": "gqa_attn_probe_hbm_read: 2 GiB read once with 16-byte loads, 4096x256 lanes, median of 3"}
+    del buf, sink
+    wg, rounds = 512, 6000
+    sinkf = torch.empty(wg * 256, dtype=torch.float32, device=dev)
+    ticks = torch.zeros(2 * wg, dtype=torch.int64, device=dev)
+    ms = timed(lambda: _lib.check(lib.gqa_attn_probe_mfma_bf16(rounds, 12345, wg, sinkf.data_ptr(), sinkf.numel(),
+                                                              ticks.data_ptr(), ticks.numel(), st.cuda_stream),
+                                  "probe_mfma_bf16"))
+    t = ticks.cpu().view(-1, 2).double()
+    ghz = float((t[:, 0] / t[:, 1]).mean()) * 0.1
+    flops = wg * 4 * rounds * 64 * 32768
+    out["mfma_bf16"] = {"value": round(flops / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "clock_ghz": round(ghz, 3),
+                        "method": "gqa_attn_probe_mfma_bf16: v_mfma_f32_32x32x16_bf16 from registers, random bf16, "
+                                  "2 waves/SIMD on every CU, median of 3"}
+    return out
+
+
 def calibration_copy(mib: int) -> None:
     """One plain device-to-device copy of a known size, run outside the timed region so a
     counter pass over this process can scale FETCH_SIZE / WRITE_SIZE to bytes."""
@@ -225,6 +277,12 @@ def main_line(args):
         },
         "device": torch.cuda.get_device_name(0),
     }
+    if args.probes:
+        roofs = measured_roofs()
+        line["roofline"]["measured_peak"] = roofs["mfma_bf16"]
+        line["roofline"]["frac_of_measured"] = round(value / roofs["mfma_bf16"]["value"], 4)
+        line["roofline_decode"]["measured_peak"] = roofs["hbm"]
+        line["roofline_decode"]["frac_of_measured"] = round(dec_gbs / roofs["hbm"]["value"], 4)
     if args.cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(S, budget_s=args.cpu_budget)
     if args.calib_copy_mb:
@@ -296,6 +354,8 @@ def main():
     ap.add_argument("--prefill-s", type=int, default=32768)
     ap.add_argument("--decode-l", type=int, default=65536)
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--no-probes", dest="probes", action="store_false",
+                    help="skip the measured HBM and MFMA roofs (gqa_attn_probe_*)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU baseline")
     ap.add_argument("--sweep", metavar="OUT_JSONL", default=None)
     ap.add_argument("--calib-copy-mb", type=int, default=0,

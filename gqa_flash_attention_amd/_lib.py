@@ -38,6 +38,9 @@ SIGNATURES = {
     "gqa_attn_decode_partials": (_c_int, [_ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
                                           _c_float, _c_int, _ptr, _c_size_t, _ptr]),
     "gqa_attn_decode_combine": (_c_int, [_ptr, _c_size_t, _ptr, _c_int, _c_int, _c_int, _c_int, _ptr]),
+    "gqa_attn_probe_hbm_read": (_c_int, [_ptr, _c_size_t, _c_int, _ptr, _c_size_t, _ptr]),
+    "gqa_attn_probe_mfma_bf16": (_c_int, [_c_int, ctypes.c_uint32, _c_int, _ptr, _c_size_t, _ptr,
+                                          _c_size_t, _ptr]),
     "gqa_attn_strerror": (ctypes.c_char_p, [_c_int]),
     "gqa_attn_last_error": (ctypes.c_char_p, []),
     "gqa_attn_release": (None, []),

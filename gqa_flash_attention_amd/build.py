@@ -23,7 +23,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libgqa_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["prefill.hip", "decode.hip", "gqa_attn_abi.cpp"]
+SOURCES = ["prefill.hip", "decode.hip", "probes.hip", "gqa_attn_abi.cpp"]
 
 ARCH = "gfx950"
 # Packed fp32 ops (v_pk_fma_f32 and friends) are disabled for all device code.

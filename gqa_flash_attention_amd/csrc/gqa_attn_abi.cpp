@@ -182,6 +182,28 @@ const char* gqa_attn_strerror(int code) {
 
 const char* gqa_attn_last_error(void) { return g_last_error.c_str(); }
 
+int gqa_attn_probe_hbm_read(const void* buf, size_t bytes, int workgroups,
+                            uint32_t* sink, size_t sink_words, void* stream) {
+  if (!buf || !sink) return GQA_ATTN_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0 || workgroups < 1 || workgroups > 65535) return GQA_ATTN_ERR_DIM;
+  if (!aligned16(buf)) return GQA_ATTN_ERR_UNSUPPORTED;
+  if (sink_words < (size_t)workgroups * 256) return GQA_ATTN_ERR_WORKSPACE;
+  const int e = gqa::launch_probe_hbm_read(buf, bytes, sink, workgroups, (hipStream_t)stream);
+  if (e != 0) return hip_fail("probe_hbm_read launch", e);
+  return GQA_ATTN_OK;
+}
+
+int gqa_attn_probe_mfma_bf16(int rounds, uint32_t seed, int workgroups,
+                             float* sink, size_t sink_floats,
+                             uint64_t* ticks, size_t ticks_count, void* stream) {
+  if (!sink || !ticks) return GQA_ATTN_ERR_NULL;
+  if (rounds < 1 || rounds > (1 << 20) || workgroups < 1 || workgroups > 65535) return GQA_ATTN_ERR_DIM;
+  if (sink_floats < (size_t)workgroups * 256 || ticks_count < (size_t)workgroups * 2) return GQA_ATTN_ERR_WORKSPACE;
+  const int e = gqa::launch_probe_mfma_bf16(rounds, seed, workgroups, sink, ticks, (hipStream_t)stream);
+  if (e != 0) return hip_fail("probe_mfma_bf16 launch", e);
+  return GQA_ATTN_OK;
+}
+
 int gqa_attn_prefill(const void* q, const void* k, const void* v, void* out,
                      int B, int S, int Hq, int Hkv, int D, float scale, int causal,
                      void* stream) {

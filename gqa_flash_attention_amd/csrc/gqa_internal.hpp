@@ -49,6 +49,11 @@ int launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
 int launch_decode(const DecodeArgs& a, bool fused, hipStream_t stream);
 int launch_decode_combine(const CombineArgs& a, hipStream_t stream);
 
+// Measurement probes (probes.hip).
+int launch_probe_hbm_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
+int launch_probe_mfma_bf16(int rounds, uint32_t seed, int workgroups, float* sink, uint64_t* ticks,
+                           hipStream_t stream);
+
 // Keys per split chosen for a decode of this shape (a multiple of 64).
 int decode_default_chunk(int B, int L, int Hkv, int G);
 // Largest accepted keys per split.

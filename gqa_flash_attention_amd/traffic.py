@@ -3,9 +3,9 @@
 Usage (each pass a separate process; see the command lines written into the summary):
 
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir_fetch> -o pmc -- \\
-        python3 bench.py --steps 5 --warmup 3 --no-cpu-baseline --calib-copy-mb 1024
+        python3 bench.py --steps 5 --warmup 3 --no-cpu-baseline --no-probes --calib-copy-mb 1024
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir_write> -o pmc -- \\
-        python3 bench.py --steps 5 --warmup 3 --no-cpu-baseline --calib-copy-mb 1024
+        python3 bench.py --steps 5 --warmup 3 --no-cpu-baseline --no-probes --calib-copy-mb 1024
     python -m gqa_flash_attention_amd.traffic <dir_fetch> <dir_write> [--copy-mb 1024]
 
 FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch. Each is scaled by the factor that
@@ -94,8 +94,8 @@ def main():
     lines = [f"# HBM traffic per launch: causal prefill S={a.prefill_s} and decode L={a.decode_l} (B=1, 32q/8kv, d=128)", "",
              "Commands (repository root, library built in-tree):", "", "```",
              "export TMPDIR=/tmp",
-             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir_fetch> -o pmc -- python3 bench.py --steps 5 --warmup 3 --no-cpu-baseline --calib-copy-mb {a.copy_mb}",
-             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir_write> -o pmc -- python3 bench.py --steps 5 --warmup 3 --no-cpu-baseline --calib-copy-mb {a.copy_mb}",
+             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir_fetch> -o pmc -- python3 bench.py --steps 5 --warmup 3 --no-cpu-baseline --no-probes --calib-copy-mb {a.copy_mb}",
+             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir_write> -o pmc -- python3 bench.py --steps 5 --warmup 3 --no-cpu-baseline --no-probes --calib-copy-mb {a.copy_mb}",
              "python -m gqa_flash_attention_amd.traffic <dir_fetch> <dir_write>", "```", "",
              f"Calibration: a {a.copy_mb} MiB device copy read FETCH_SIZE = {cal['fetch_kib']:.0f} KiB and "
              f"WRITE_SIZE = {cal['write_kib']:.0f} KiB, so the scale factors are {cal['fetch_scale']:.3f} (fetch) "

@@ -145,6 +145,40 @@ int gqa_attn_decode_partials(const void* q, const void* kcache, const void* vcac
 int gqa_attn_decode_combine(const void* ws, size_t ws_bytes, void* out,
                             int B, int Hq, int D, int nsplit, void* stream);
 
+/*
+ * Measured roofline denominators. The metakernel page ("How it works", "Return
+ * schemas") derives device limits from dedicated probe kernels, each reported
+ * with the clock it ran at, instead of spec-sheet figures. These two are the
+ * limits of the two attention kernels. The caller times each call (for example
+ * with events on `stream`); neither allocates.
+ *
+ * Cold HBM read rate: every byte of buf is read once with 16-byte loads.
+ *   buf        : device, 16-byte aligned; bytes > 0 and a multiple of 16. A buffer
+ *                several times the 256 MB MALL measures HBM, not the cache.
+ *   workgroups : 1..65535 workgroups of 256 lanes (4096 suits MI355X).
+ *   sink       : device uint32 [sink_words], sink_words >= 256 * workgroups; one
+ *                XOR of the data per lane (only there so the loads are kept).
+ */
+int gqa_attn_probe_hbm_read(const void* buf, size_t bytes, int workgroups,
+                            uint32_t* sink, size_t sink_words, void* stream);
+
+/*
+ * Register-resident bf16 MFMA rate: workgroups of 4 waves, 2 waves per SIMD,
+ * each wave issuing rounds x 64 v_mfma_f32_32x32x16_bf16 (32768 flop each) on 8
+ * independent fp32 accumulators, operands random bf16 (seeded) so every
+ * instruction sees new data. Flops per call:
+ *     workgroups * 4 * rounds * 64 * 32768.
+ *   rounds     : 1..1048576;  workgroups : 1..65535 (512 = 2 per CU).
+ *   sink       : device float [sink_floats], sink_floats >= 256 * workgroups.
+ *   ticks      : device uint64 [ticks_count], ticks_count >= 2 * workgroups.
+ *                Workgroup w writes ticks[2w] = shader-clock cycles of its MFMA
+ *                loop (s_memtime) and ticks[2w+1] = the same interval in 100 MHz
+ *                ticks (s_memrealtime): their ratio x 0.1 GHz is the clock it ran at.
+ */
+int gqa_attn_probe_mfma_bf16(int rounds, uint32_t seed, int workgroups,
+                             float* sink, size_t sink_floats,
+                             uint64_t* ticks, size_t ticks_count, void* stream);
+
 /* Static description of a return code. Never NULL. */
 const char* gqa_attn_strerror(int code);
 

@@ -135,3 +135,23 @@ def test_decode_plan_and_workspace_size(lib):
 
 def test_release_without_any_workspace_is_harmless(lib):
     lib.gqa_attn_release()
+
+
+def test_probe_argument_errors(lib):
+    # HBM read probe: buf, bytes (multiple of 16), workgroups, sink (>= 256 words per workgroup)
+    assert lib.gqa_attn_probe_hbm_read(None, 1024, 4, P, 1024, None) == _lib.ERR_NULL
+    assert lib.gqa_attn_probe_hbm_read(P, 1024, 4, None, 1024, None) == _lib.ERR_NULL
+    assert lib.gqa_attn_probe_hbm_read(P, 0, 4, P, 1024, None) == _lib.ERR_DIM
+    assert lib.gqa_attn_probe_hbm_read(P, 1000, 4, P, 1024, None) == _lib.ERR_DIM
+    assert lib.gqa_attn_probe_hbm_read(P, 1024, 0, P, 1024, None) == _lib.ERR_DIM
+    assert lib.gqa_attn_probe_hbm_read(P, 1024, 65536, P, 1 << 30, None) == _lib.ERR_DIM
+    assert lib.gqa_attn_probe_hbm_read(MIS, 1024, 4, P, 1024, None) == _lib.ERR_UNSUPPORTED
+    assert lib.gqa_attn_probe_hbm_read(P, 1024, 4, P, 1023, None) == _lib.ERR_WORKSPACE
+    # MFMA probe: rounds, seed, workgroups, sink (>= 256 per workgroup), ticks (>= 2 per workgroup)
+    assert lib.gqa_attn_probe_mfma_bf16(8, 1, 512, None, 1 << 17, P, 1024, None) == _lib.ERR_NULL
+    assert lib.gqa_attn_probe_mfma_bf16(8, 1, 512, P, 1 << 17, None, 1024, None) == _lib.ERR_NULL
+    assert lib.gqa_attn_probe_mfma_bf16(0, 1, 512, P, 1 << 17, P, 1024, None) == _lib.ERR_DIM
+    assert lib.gqa_attn_probe_mfma_bf16((1 << 20) + 1, 1, 512, P, 1 << 17, P, 1024, None) == _lib.ERR_DIM
+    assert lib.gqa_attn_probe_mfma_bf16(8, 1, 0, P, 1 << 17, P, 1024, None) == _lib.ERR_DIM
+    assert lib.gqa_attn_probe_mfma_bf16(8, 1, 512, P, (1 << 17) - 1, P, 1024, None) == _lib.ERR_WORKSPACE
+    assert lib.gqa_attn_probe_mfma_bf16(8, 1, 512, P, 1 << 17, P, 1023, None) == _lib.ERR_WORKSPACE
