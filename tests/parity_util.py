@@ -31,11 +31,45 @@ def errors(got: np.ndarray, want: np.ndarray):
     return float(d.max()), float(d.mean())
 
 
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |x| (8 significand bits); the smallest normal's for 0."""
+    a = np.maximum(np.abs(x), np.float64(2.0) ** -126)
+    return np.float64(2.0) ** (np.floor(np.log2(a)) - 7)
+
+
+def compare(got: np.ndarray, want: np.ndarray) -> dict:
+    """Diagnostic report of a GPU result against the fp64 oracle: error measures, NaN/Inf
+    counts, the first element past TOL_MAX (flat index) and a histogram of the distance
+    to the oracle's own bf16 rounding, in bf16 ulps of that rounded value."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    d = np.abs(got - want)
+    r = oracle.round_to_bf16(want)
+    ulps = np.abs(got - r) / bf16_ulp(r)
+    bad = np.flatnonzero(~(d <= TOL_MAX))
+    edges = [0, 1, 2, 4, 16]
+    hist = {"0": int(np.sum(ulps == 0))}
+    for lo, hi in zip(edges[:-1], edges[1:]):
+        hist[f"({lo},{hi}]"] = int(np.sum((ulps > lo) & (ulps <= hi)))
+    hist[f">{edges[-1]}"] = int(np.sum(ulps > edges[-1]))
+    rel = d / np.maximum(np.abs(want), 1e-6)
+    return {
+        "n": int(d.size), "max_abs": float(np.nanmax(d)) if d.size else 0.0,
+        "mean_abs": float(np.nanmean(d)) if d.size else 0.0,
+        "max_rel_where_abs_ge_1e-2": float(np.max(rel[np.abs(want) >= 1e-2])) if np.any(np.abs(want) >= 1e-2) else 0.0,
+        "nan": int(np.isnan(got).sum()), "inf": int(np.isinf(got).sum()),
+        "first_past_tol": int(bad[0]) if bad.size else None,
+        "ulp_hist_vs_bf16_oracle": hist,
+    }
+
+
 def assert_close(got: np.ndarray, want: np.ndarray, what: str = ""):
     mx, mean = errors(got, want)
     floor_mx, floor_mean = errors(oracle.round_to_bf16(want), want)
+    rep = compare(got, want)
     msg = (f"{what}: max abs err {mx:.3e} (tol {TOL_MAX}), mean {mean:.3e} (tol {TOL_MEAN}); "
-           f"bf16 rounding floor max {floor_mx:.3e} mean {floor_mean:.3e}")
+           f"bf16 rounding floor max {floor_mx:.3e} mean {floor_mean:.3e}; "
+           f"ulps vs bf16(oracle) {rep['ulp_hist_vs_bf16_oracle']}")
     print(msg, flush=True)
     assert mx <= TOL_MAX and mean <= TOL_MEAN, msg
     return mx, mean
