@@ -22,6 +22,7 @@ the 256 MB MALL, so every decode reads its cache from HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-probes]
     python bench.py --sweep out.jsonl     # every prefill/decode size, one JSON line each
+    python bench.py --sweep-chunks out.jsonl   # decode split sizes, paired timing
 """
 
 from __future__ import annotations
@@ -164,6 +165,80 @@ def run_step_timing(S, L, steps, warmup):
     pf = sorted(ev[i][0].elapsed_time(ev[i][1]) for i in range(steps))
     dc = sorted(ev[i][1].elapsed_time(ev[i][2]) for i in range(steps))
     return wall, pf, dc
+
+
+SWEEP_CHUNK_L = (16384, 32768, 65536)
+
+
+def chunk_candidates(L: int):
+    """Split sizes the decode chunk sweep visits at cache length L (B = 1): the library's
+    own choice plus every power of two times 64 from 128 to 16384. Returns (default,
+    runnable, not_run) where not_run lists (chunk, reason) for points that are not timed."""
+    import gqa_flash_attention_amd as gqa
+    default, _ = gqa.decode_plan(1, L, 32, 8, 128)
+    pts = sorted({default} | {64 * 2 ** i for i in range(1, 9)})
+    run, skip = [], []
+    for c in pts:
+        if c > L:
+            skip.append((c, "longer than the cache: the single split that chunk = L already gives"))
+        else:
+            run.append(c)
+    return default, run, skip
+
+
+def sweep_chunks(path: str, rounds: int = 8):
+    """Decode split-size sweep at B = 1 (SWEEP_CHUNK_L): every runnable point of
+    chunk_candidates() timed in paired rounds (the points alternate in rotated order,
+    caches rotated over >= 1 GB so the MALL holds none), median time per point and the
+    median of per-round ratios against the library's default chunk. Parity of every
+    point against the oracle is checked by tests/test_sweep_points_gpu.py on the same
+    seeded inputs and points."""
+    import statistics
+    import torch
+    import gqa_flash_attention_amd as gqa
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    with open(path, "w") as f:
+        for L in SWEEP_CHUNK_L:
+            default, run, skip = chunk_candidates(L)
+            _, qd, kc, vc, lens = [None] + make_inputs(64, L, dev)[3:]
+            per = 2 * L * 8 * 128 * 2
+            nc = max(4, min(64, -(-(1 << 30) // per)))
+            kcs = [kc.clone() for _ in range(nc)]
+            vcs = [vc.clone() for _ in range(nc)]
+            out = torch.empty_like(qd)
+            wss = {c: torch.zeros(gqa.decode_workspace_bytes(1, L, 32, 8, 128, c), dtype=torch.uint8, device=dev)
+                   for c in run}
+            call = lambda c, i: gqa.decode(qd, kcs[i % nc], vcs[i % nc], lens, out=out, chunk=c, workspace=wss[c])
+            for c in run:
+                for i in range(2 * nc):
+                    call(c, i)
+            torch.cuda.synchronize()
+            times = {c: [] for c in run}
+            for r in range(rounds):
+                order = run[r % len(run):] + run[:r % len(run)]
+                for c in order:
+                    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nc)]
+                    for i in range(nc):
+                        ev[i][0].record(st)
+                        call(c, i)
+                        ev[i][1].record(st)
+                    torch.cuda.synchronize()
+                    times[c].append(statistics.median(a.elapsed_time(b) for a, b in ev))
+            for c in run:
+                t = statistics.median(times[c])
+                ratio = statistics.median(times[default][i] / times[c][i] for i in range(rounds))
+                row = {"mode": "decode_chunk", "L": L, "chunk": c, "nsplit": -(-L // c), "default": c == default,
+                       "status": "run", "us_median": round(t * 1e3, 2), "GBs": round(decode_bytes(L) / (t * 1e-3) / 1e9),
+                       "speed_vs_default": round(ratio, 3)}
+                print(json.dumps(row), flush=True)
+                f.write(json.dumps(row) + "\n")
+            for c, why in skip:
+                row = {"mode": "decode_chunk", "L": L, "chunk": c, "status": "not_run", "reason": why}
+                print(json.dumps(row), flush=True)
+                f.write(json.dumps(row) + "\n")
+            del kcs, vcs, wss
+            torch.cuda.empty_cache()
 
 
 def measured_roofs():
@@ -358,6 +433,8 @@ def main():
                     help="skip the measured HBM and MFMA roofs (gqa_attn_probe_*)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU baseline")
     ap.add_argument("--sweep", metavar="OUT_JSONL", default=None)
+    ap.add_argument("--sweep-chunks", metavar="OUT_JSONL", default=None,
+                    help="decode split-size sweep with paired timing (see sweep_chunks)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, one device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -371,6 +448,8 @@ def main():
         sys.exit(2)
     if args.sweep:
         sweep(args.sweep, args.steps, args.warmup)
+    elif args.sweep_chunks:
+        sweep_chunks(args.sweep_chunks)
     else:
         main_line(args)
 
