@@ -13,12 +13,21 @@
 //    The last workgroup of a (sequence, KV head) to finish merges the partials of all
 //    chunks; with a single chunk the result is written directly.
 //
-// Streaming. A workgroup walks its chunk in 64-key tiles through an LDS ring of NSTAGE
-// stages (K 16 KB + V 16 KB each). Tiles are copied with global_load_lds_dwordx4 straight
-// from HBM into LDS, NSTAGE-1 tiles ahead, so ~96 KB per CU stay in flight with no
-// register cost. Rows at or past lens[b] are never requested: their addresses are
-// redirected to the last valid row. The library sizes chunks so that a batch-1 decode is
-// about one workgroup per CU, each streaming one contiguous slab of the cache.
+// Streaming. A workgroup walks its split's keys in 64-key tiles through an LDS ring of
+// NSTAGE stages (K 16 KB + V 16 KB each). Tiles are copied with global_load_lds_dwordx4
+// straight from HBM into LDS, NSTAGE-1 tiles ahead, so ~96 KB per CU stay in flight with
+// no register cost. Rows at or past lens[b] are never requested: their addresses are
+// redirected to the last valid row. The library sizes splits so that a batch-1 decode is
+// about one workgroup per CU. Which tiles a split holds depends on the entry point:
+//  - the stand-alone partials: split s is the chunk [s*chunk, (s+1)*chunk), walked from
+//    its tile 5s (mod its tile count) round, so that the reads in flight at one moment
+//    are not all at one offset into slabs a chunk apart (~4% slower on MI355X for a
+//    pure-read kernel of the batch-1, 64K-key shape). Only the summation order changes;
+//  - the fused decode, whose partials never leave the kernel: split s takes tiles s,
+//    s + nsplit, s + 2 nsplit, ... of the whole sequence, so at any moment the
+//    workgroups of a head read one contiguous stretch of the cache (a further 1-4% for
+//    the same pure-read kernel at 16K-64K keys), and a short sequence in a batch spreads
+//    over all its splits instead of leaving the last ones empty.
 //
 // Arithmetic per wave (16 keys of each tile): S^T (16 keys x 16 heads; 4 heads are real
 // for Llama-3-8B) = K Q^T with v_mfma_f32_16x16x32_bf16, K from LDS as the A operand and
@@ -56,9 +65,19 @@ __device__ __forceinline__ void publish(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// FUSE: merge the chunks in the last-arriving workgroup (and write bf16 out); otherwise
-// only write the per-chunk partials.
-template <int NSTAGE, bool FUSE>
+// Device-coherent 16-byte load: a buffer load with the agent-scope coherence bit (sc1),
+// the encoding of a relaxed agent-scope atomic load. Offsets past the resource's size
+// read zero.
+constexpr int kBufferDword3 = 0x00020000;   // raw 32-bit buffer resource word 3 on gfx9
+constexpr int kCachePolicySC1 = 16;
+__device__ __forceinline__ f32x4 load_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kCachePolicySC1));
+}
+
+// FUSE: merge the splits in the last-arriving workgroup (and write bf16 out); otherwise
+// only write the per-split partials. STRIDED: the tile-to-split assignment of the fused
+// decode (see the top of this file); otherwise contiguous chunks.
+template <int NSTAGE, bool FUSE, bool STRIDED>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   static_assert(NSTAGE >= 2 && NSTAGE <= 5, "ring depth");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * 2 * kTileBytes];
@@ -77,18 +96,32 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   int len = a.lens[b];
   len = len < 0 ? 0 : (len > a.L ? a.L : len);
-  const int key_begin = split * a.chunk;
-  const int nkeys = min(a.chunk, len - key_begin);
+  int ntiles, rot = 0;
+  if (STRIDED) {
+    const int T = (len + kTileRows - 1) / kTileRows;   // tiles of the sequence
+    ntiles = split < T ? (T - 1 - split) / a.nsplit + 1 : 0;
+  } else {
+    const int nkeys = min(a.chunk, len - split * a.chunk);
+    ntiles = nkeys > 0 ? (nkeys + kTileRows - 1) / kTileRows : 0;
+    rot = ntiles > 0 ? (5 * split) % ntiles : 0;
+  }
+  // First key (counted from the start of the sequence) of the t-th tile this workgroup
+  // streams. Chunks are whole tiles, so the only partial tile is the one holding key
+  // len - 1, and a tile starting at key k holds min(64, len - k) keys.
+  auto tile_key = [&](int t) {
+    if (STRIDED) return (t * a.nsplit + split) * kTileRows;
+    const int p = t + rot < ntiles ? t + rot : t + rot - ntiles;
+    return split * a.chunk + p * kTileRows;
+  };
   const int hbase = 16 * hg;
   const int nheads = min(16, a.G - hbase);
   const size_t head0 = (size_t)b * a.Hq + (size_t)g * a.G + hbase;   // first served head row
   float* lse_out = a.lse + head0 * a.nsplit + split;
   float* opart = a.o_part + (head0 * a.nsplit + split) * kD;
 
-  if (nkeys > 0) {
-    const int ntiles = (nkeys + kTileRows - 1) / kTileRows;
+  if (ntiles > 0) {
     const size_t kv_stride = (size_t)a.Hkv * kD;
-    const size_t row0 = ((size_t)b * a.L + key_begin) * a.Hkv + g;
+    const size_t row0 = (size_t)b * a.L * a.Hkv + g;
     const uint16_t* kbase = a.kc + row0 * kD;
     const uint16_t* vbase = a.vc + row0 * kD;
     GQA_LDS uint8_t* const ring = (GQA_LDS uint8_t*)lds;
@@ -104,17 +137,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
     TileCopy<kDecWaves> copy;
     copy.init(kv_stride, wave, lane);
-    // Copies of tile t (K then V): per-lane offsets for a full tile, the clamped per-row
-    // path for the ragged last tile.
+    // Copies of the t-th streamed tile (K then V): per-lane offsets for a full tile, the
+    // clamped per-row path for the ragged last tile.
     auto issue = [&](int t) {
       GQA_LDS uint8_t* st = ring + (t % NSTAGE) * (2 * kTileBytes);
-      const int r0 = t * kTileRows;
+      const int r0 = tile_key(t);
       const size_t off = (size_t)r0 * kv_stride;
-      if (nkeys - r0 >= kTileRows) {
+      if (len - r0 >= kTileRows) {
         copy.issue_full(st, st + kTileBytes, kbase + off, vbase + off, wave);
       } else {
-        stage_tile<kDecWaves, false>(st, kbase + off, kv_stride, nkeys - r0, wave, lane);
-        stage_tile<kDecWaves, true>(st + kTileBytes, vbase + off, kv_stride, nkeys - r0, wave, lane);
+        stage_tile<kDecWaves, false>(st, kbase + off, kv_stride, len - r0, wave, lane);
+        stage_tile<kDecWaves, true>(st + kTileBytes, vbase + off, kv_stride, len - r0, wave, lane);
       }
     };
     for (int t = 0; t < NSTAGE - 1; ++t)
@@ -143,8 +176,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
       if (t + NSTAGE - 1 < ntiles) issue(t + NSTAGE - 1);
 
-      const int kw = t * kTileRows + 16 * wave;   // chunk-relative first key of this wave
-      if (kw < nkeys) {
+      const int kw = tile_key(t) + 16 * wave;   // first key of this wave
+      if (kw < len) {
         const GQA_LDS uint8_t* kt = ring + (t % NSTAGE) * (2 * kTileBytes);
         const GQA_LDS uint8_t* vt = kt + kTileBytes;
         f32x4 s = f32x4{};
@@ -156,7 +189,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         float mx = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          x[v] = (kw + 4 * grp + v < nkeys) ? s[v] * c : -INFINITY;
+          x[v] = (kw + 4 * grp + v < len) ? s[v] * c : -INFINITY;
           mx = fmaxf(mx, x[v]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -188,38 +221,49 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     l_part = halves_sum(l_part);
 
     // Merge the waves through LDS (every copy has landed: the last wait was vmcnt(0)).
+    // Rows of 132 floats put the 16 lanes of a 16-byte write on distinct banks.
     __syncthreads();
-    GQA_LDS float* wo = (GQA_LDS float*)lds;       // [4][16][128] per-wave O
-    GQA_LDS float* wm = wo + kDecWaves * 16 * kD;  // [4][16] per-wave max
+    constexpr int kWo = kD + 4;
+    GQA_LDS float* wo = (GQA_LDS float*)lds;       // [4][16][kWo] per-wave O, real heads only
+    GQA_LDS float* wm = wo + kDecWaves * 16 * kWo; // [4][16] per-wave max
     GQA_LDS float* wl = wm + kDecWaves * 16;       // [4][16] per-wave sum
+    if (n < nheads) {
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) wo[(wave * 16 + n) * kD + 16 * mb + 4 * grp + v] = oacc[mb][v];
-    if (grp == 0) {
-      wm[wave * 16 + n] = m_run;
-      wl[wave * 16 + n] = l_part;
+      for (int mb = 0; mb < 8; ++mb)
+        *(GQA_LDS f32x4*)(wo + (wave * 16 + n) * kWo + 16 * mb + 4 * grp) = oacc[mb];
+      if (grp == 0) {
+        wm[wave * 16 + n] = m_run;
+        wl[wave * 16 + n] = l_part;
+      }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < nheads * kD; idx += 256) {
-      const int hn = idx / kD;
-      const int d = idx % kD;
+    // thread -> (head, 4 consecutive d)
+    for (int col = threadIdx.x; col < nheads * (kD / 4); col += 256) {
+      const int hn = col / (kD / 4);
+      const int d4 = 4 * (col % (kD / 4));
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, wm[w * 16 + hn]);
-      float num = 0.f, den = 0.f;
+      f32x4 num = f32x4{};
+      float den = 0.f;
 #pragma unroll
       for (int w = 0; w < kDecWaves; ++w) {
         const float mw = wm[w * 16 + hn];
         const float sc = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
-        num += sc * wo[(w * 16 + hn) * kD + d];
+        num += sc * *(const GQA_LDS f32x4*)(wo + (w * 16 + hn) * kWo + d4);
         den += sc * wl[w * 16 + hn];
       }
       if (FUSE && a.nsplit == 1) {
-        a.out[(head0 + hn) * kD + d] = bf16_bits(num / den);
+        typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+        u16x4 o;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[v] = bf16_bits(num[v] / den);
+        *(u16x4*)(a.out + (head0 + hn) * kD + d4) = o;
       } else {
-        publish(opart + (size_t)hn * a.nsplit * kD + d, num / den);
-        if (d == 0) publish(lse_out + (size_t)hn * a.nsplit, M + log2f(den));
+        float* dst = opart + (size_t)hn * a.nsplit * kD + d4;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) publish(dst + v, num[v] / den);
+        if (d4 == 0) publish(lse_out + (size_t)hn * a.nsplit, M + log2f(den));
       }
     }
   } else {
@@ -233,29 +277,28 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   if (!FUSE || a.nsplit == 1) return;
 
   // Count this chunk. The partial was written with device-coherent stores, and the
-  // barrier below waits for them to complete (vmcnt(0)) before the count, so the
-  // workgroup that counts last sees every chunk's partial. It merges them and resets
-  // the counter for the next call. No workgroup ever waits for another.
+  // barrier below waits for them to complete (vmcnt(0)) before the count, so when the
+  // last workgroup's count returns, every chunk's partial is in memory. That workgroup
+  // merges them, reading with device-coherent loads (which cannot hit a stale line in
+  // its XCD's L2, so no cache-wide invalidation is needed), and afterwards resets the
+  // counter for the next call. No workgroup ever waits for another.
   __syncthreads();
   int* counter = a.counters + (size_t)b * a.Hkv * a.hgroups + gy;
   if (threadIdx.x == 0)
     s_last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.nsplit - 1);
   __syncthreads();
   if (!s_last) return;
-  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // Drop any stale copy of the partials from this XCD's caches, then read them with
-  // ordinary 16-byte loads.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-  // out[h, d] = sum_s 2^(lse_s - M) o_s[d] / sum_s 2^(lse_s - M), merged with a running
-  // maximum. Thread -> (head, 4 consecutive d) column and a share of the chunks; each
-  // thread fetches kBatch chunks at once so the loads overlap.
+  // out[h, d] = sum_s 2^(lse_s - M) o_s[d] / sum_s 2^(lse_s - M). Thread -> (head, 4
+  // consecutive d) column and a share of the chunks, kBatch chunks per round of loads;
+  // within a round one maximum and independent weights, across rounds a rescale.
   constexpr int kBatch = 16;
   const int ncols = nheads * (kD / 4);
   const int nparts = ncols >= 256 ? 1 : 256 / ncols;
   GQA_LDS float* red = (GQA_LDS float*)lds;      // [nparts][ncols][6]
   const float* lse_all = a.lse + head0 * a.nsplit;
-  const float* o_all = a.o_part + head0 * a.nsplit * kD;
+  const __amdgpu_buffer_rsrc_t o_all = __builtin_amdgcn_make_buffer_rsrc(
+      a.o_part + head0 * a.nsplit * kD, (short)0, nheads * a.nsplit * kD * 4, kBufferDword3);
   for (int base = 0; base < ncols * nparts; base += 256) {
     const int u = base + threadIdx.x;
     const bool act = u < ncols * nparts;
@@ -267,27 +310,38 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     f32x4 num = f32x4{};
     if (act) {
       const float* lrow = lse_all + (size_t)hn * a.nsplit;
-      const float* orow = o_all + (size_t)hn * a.nsplit * kD + d4;
+      const uint32_t orow = (uint32_t)((hn * a.nsplit * kD + d4) * 4);
       for (int s0 = part; s0 < a.nsplit; s0 += kBatch * nparts) {
         float lv[kBatch];
         f32x4 ov[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-          const int s = s0 + j * nparts;
-          const bool in = s < a.nsplit;
-          lv[j] = in ? lrow[s] : -INFINITY;
-          ov[j] = in ? *(const f32x4*)(orow + (size_t)s * kD) : f32x4{};
+          const int s = min(s0 + j * nparts, a.nsplit - 1);
+          lv[j] = __hip_atomic_load(lrow + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ov[j] = load_coherent16(o_all, orow + (uint32_t)s * (kD * 4));
+        }
+        float mb = m;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          // past the last chunk, or an empty chunk (lse = -inf, o_part row never written)
+          if (s0 + j * nparts >= a.nsplit || lv[j] == -INFINITY) {
+            lv[j] = -INFINITY;
+            ov[j] = f32x4{};
+          }
+          mb = fmaxf(mb, lv[j]);
+        }
+        if (mb == -INFINITY) continue;
+        if (mb > m) {
+          const float sc = exp2_fast(m - mb);   // 0 while nothing has been folded
+          num *= sc;
+          den *= sc;
+          m = mb;
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-          // An empty chunk (lse = -inf) has no partial: its o_part row is never used.
-          if (lv[j] == -INFINITY) continue;
-          const float mn = fmaxf(m, lv[j]);
-          const float sc_old = (m == -INFINITY) ? 0.f : exp2_fast(m - mn);
-          const float w = exp2_fast(lv[j] - mn);
-          num = num * sc_old + ov[j] * w;
-          den = den * sc_old + w;
-          m = mn;
+          const float w = exp2_fast(lv[j] - m);
+          num += w * ov[j];
+          den += w;
         }
       }
     }
@@ -326,6 +380,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       *(u16x4*)(a.out + (head0 + hn) * kD + d4) = w;
     }
   }
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Stand-alone merge of per-chunk partials (the second half of a decode on its own):
@@ -392,8 +447,8 @@ int decode_default_chunk(int B, int L, int Hkv, int G) {
 
 int launch_decode(const DecodeArgs& a, bool fused, hipStream_t stream) {
   const dim3 grid((unsigned)a.nsplit, (unsigned)(a.Hkv * a.hgroups), (unsigned)a.B);
-  if (fused) hipLaunchKernelGGL((decode_kernel<4, true>), grid, dim3(256), 0, stream, a);
-  else       hipLaunchKernelGGL((decode_kernel<4, false>), grid, dim3(256), 0, stream, a);
+  if (fused) hipLaunchKernelGGL((decode_kernel<4, true, true>), grid, dim3(256), 0, stream, a);
+  else       hipLaunchKernelGGL((decode_kernel<4, false, false>), grid, dim3(256), 0, stream, a);
   return (int)hipGetLastError();
 }
 

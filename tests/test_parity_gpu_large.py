@@ -73,8 +73,9 @@ def test_decode_cache_past_2pow31_elements():
         assert np.mean(np.abs(og - o_ref[0, :, 0])) < 2e-3, (b, c)
         lg = lse[b, :, c].cpu().double().numpy()
         assert np.max(np.abs(lg - lse_ref[0, :, 0] / np.log(2.0))) < 2e-2, (b, c)
-    # the fused single-launch decode reaches the same slots: it must agree with the
-    # stand-alone merge of the split results up to the merge's summation order
+    # the fused single-launch decode assigns keys to splits its own way (strided tiles);
+    # it must agree with the stand-alone merge of the chunk results up to summation
+    # order: the outputs here are ~1e-3 in size, so 1e-4 is a few of their bf16 ulps
     split_out = gqa.decode_combine(ws, B, HQ, nsplit)
     fused = gqa.decode(q, kc, vc, lens, chunk=chunk)
     auto = gqa.decode(q, kc, vc, lens)
