@@ -65,13 +65,16 @@ __device__ __forceinline__ void publish(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Device-coherent 16-byte load: a buffer load with the agent-scope coherence bit (sc1),
-// the encoding of a relaxed agent-scope atomic load. Offsets past the resource's size
-// read zero.
+// Device-coherent 16-byte load and store: buffer accesses with the agent-scope coherence
+// bit (sc1), the encoding of relaxed agent-scope atomic loads and stores. Offsets past
+// the resource's size read zero and are not written.
 constexpr int kBufferDword3 = 0x00020000;   // raw 32-bit buffer resource word 3 on gfx9
 constexpr int kCachePolicySC1 = 16;
 __device__ __forceinline__ f32x4 load_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kCachePolicySC1));
+}
+__device__ __forceinline__ void store_coherent16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)byte_off, 0, kCachePolicySC1);
 }
 
 // FUSE: merge the splits in the last-arriving workgroup (and write bf16 out); otherwise
@@ -117,7 +120,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int nheads = min(16, a.G - hbase);
   const size_t head0 = (size_t)b * a.Hq + (size_t)g * a.G + hbase;   // first served head row
   float* lse_out = a.lse + head0 * a.nsplit + split;
-  float* opart = a.o_part + (head0 * a.nsplit + split) * kD;
+  // o_part rows of the served heads: [nheads][nsplit][kD] fp32
+  const __amdgpu_buffer_rsrc_t o_rows = __builtin_amdgcn_make_buffer_rsrc(
+      a.o_part + head0 * a.nsplit * kD, (short)0, (int)((uint32_t)nheads * (uint32_t)a.nsplit * (kD * 4u)),
+      kBufferDword3);
 
   if (ntiles > 0) {
     const size_t kv_stride = (size_t)a.Hkv * kD;
@@ -260,9 +266,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         for (int v = 0; v < 4; ++v) o[v] = bf16_bits(num[v] / den);
         *(u16x4*)(a.out + (head0 + hn) * kD + d4) = o;
       } else {
-        float* dst = opart + (size_t)hn * a.nsplit * kD + d4;
+        f32x4 o;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) publish(dst + v, num[v] / den);
+        for (int v = 0; v < 4; ++v) o[v] = num[v] / den;
+        store_coherent16(o_rows, (uint32_t)(((hn * a.nsplit + split) * kD + d4) * 4), o);
         if (d4 == 0) publish(lse_out + (size_t)hn * a.nsplit, M + log2f(den));
       }
     }
@@ -297,8 +304,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int nparts = ncols >= 256 ? 1 : 256 / ncols;
   GQA_LDS float* red = (GQA_LDS float*)lds;      // [nparts][ncols][6]
   const float* lse_all = a.lse + head0 * a.nsplit;
-  const __amdgpu_buffer_rsrc_t o_all = __builtin_amdgcn_make_buffer_rsrc(
-      a.o_part + head0 * a.nsplit * kD, (short)0, nheads * a.nsplit * kD * 4, kBufferDword3);
   for (int base = 0; base < ncols * nparts; base += 256) {
     const int u = base + threadIdx.x;
     const bool act = u < ncols * nparts;
@@ -318,7 +323,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         for (int j = 0; j < kBatch; ++j) {
           const int s = min(s0 + j * nparts, a.nsplit - 1);
           lv[j] = __hip_atomic_load(lrow + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ov[j] = load_coherent16(o_all, orow + (uint32_t)s * (kD * 4));
+          ov[j] = load_coherent16(o_rows, orow + (uint32_t)s * (kD * 4));
         }
         float mb = m;
 #pragma unroll

@@ -66,7 +66,9 @@ DecodeShapeCheck check_decode_shape(int B, int L, int Hq, int Hkv, int D, float 
   if (chunk == 0) chunk = gqa::decode_default_chunk(B, L, Hkv, G);
   if (chunk < 64 || chunk % 64 != 0 || chunk > gqa::kMaxChunk) { r.code = GQA_ATTN_ERR_WORKSPACE; return r; }
   r.chunk = chunk;
-  r.nsplit = (int)(((long long)L + chunk - 1) / chunk);
+  const long long nsplit = ((long long)L + chunk - 1) / chunk;
+  if (nsplit > gqa::kMaxSplits) { r.code = GQA_ATTN_ERR_WORKSPACE; return r; }
+  r.nsplit = (int)nsplit;
   if (elems4(B, Hq, r.nsplit) < 0) { r.code = GQA_ATTN_ERR_DIM; return r; }
   return r;
 }
@@ -293,6 +295,7 @@ int gqa_attn_decode_combine(const void* ws, size_t ws_bytes, void* out,
                             int B, int Hq, int D, int nsplit, void* stream) {
   if (!ws || !out) return GQA_ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || nsplit < 1) return GQA_ATTN_ERR_DIM;
+  if (nsplit > gqa::kMaxSplits) return GQA_ATTN_ERR_WORKSPACE;
   if (D != 128) return GQA_ATTN_ERR_UNSUPPORTED;
   if (elems4(B, Hq, nsplit) < 0 || B > kMaxGridY || Hq > kMaxGridY) return GQA_ATTN_ERR_DIM;
   if (!aligned16(ws) || !aligned16(out)) return GQA_ATTN_ERR_UNSUPPORTED;

@@ -58,5 +58,8 @@ int launch_probe_mfma_bf16(int rounds, uint32_t seed, int workgroups, float* sin
 int decode_default_chunk(int B, int L, int Hkv, int G);
 // Largest accepted keys per split.
 constexpr int kMaxChunk = 1 << 24;
+// Most splits per sequence: the partials of one (sequence, KV head), up to 16 heads x
+// nsplit x 512 B, then span at most 2 GiB and are addressed with 32-bit byte offsets.
+constexpr int kMaxSplits = 1 << 18;
 
 }  // namespace gqa

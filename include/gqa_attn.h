@@ -94,6 +94,9 @@ int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
  * The split the library would choose for a decode of this shape.
  * On success writes the keys per split (*chunk, a multiple of 64) and the
  * number of splits (*nsplit = ceil(L / chunk)). Either output may be NULL.
+ * Every decode entry point accepts at most 262144 splits (2^18) and returns
+ * GQA_ATTN_ERR_WORKSPACE beyond that; the library's own choice stays within
+ * it for every L up to 2^30.
  */
 int gqa_attn_decode_plan(int B, int L, int Hq, int Hkv, int D, int* chunk, int* nsplit);
 
@@ -110,7 +113,8 @@ size_t gqa_attn_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int D, int
 /*
  * Decode with a caller-owned workspace and an explicit split size. Same
  * semantics as gqa_attn_decode. chunk = 0 takes the library's choice;
- * otherwise chunk must be a positive multiple of 64. ws must be 16-byte
+ * otherwise chunk must be a positive multiple of 64 with ceil(L / chunk) at
+ * most 2^18. ws must be 16-byte
  * aligned and hold at least gqa_attn_decode_workspace_bytes(..., chunk) bytes.
  * The counters part of ws (its first max(4096, B*Hq) int32) must hold zeros
  * before the call: allocate the buffer zeroed; each completed call leaves the

@@ -111,6 +111,15 @@ def test_decode_ws_and_split_errors(lib):
     assert lib.gqa_attn_decode_combine(None, 10, P, 1, 32, 128, 8, None) == _lib.ERR_NULL
     assert lib.gqa_attn_decode_combine(P, 10 ** 9, P, 1, 32, 64, 8, None) == _lib.ERR_UNSUPPORTED
     assert lib.gqa_attn_decode_combine(P, 10 ** 9, P, 1, 32, 128, 0, None) == _lib.ERR_DIM
+    # at most 2^18 splits per sequence, so one (sequence, KV head)'s partials fit 32-bit offsets
+    big = (1 << 24) + 64   # 2^18 + 1 splits of 64 keys
+    assert lib.gqa_attn_decode_workspace_bytes(1, big, 32, 8, 128, 64) == 0
+    assert lib.gqa_attn_decode_workspace_bytes(1, big, 32, 8, 128, 128) > 0
+    rc = lib.gqa_attn_decode_ws(P, P, P, P, P, 1, big, 32, 8, 128, 0.088, 64, P, 1 << 40, None)
+    assert rc == _lib.ERR_WORKSPACE
+    rc = lib.gqa_attn_decode_partials(P, P, P, P, 1, big, 32, 8, 128, 0.088, 64, P, 1 << 40, None)
+    assert rc == _lib.ERR_WORKSPACE
+    assert lib.gqa_attn_decode_combine(P, 1 << 40, P, 1, 32, 128, (1 << 18) + 1, None) == _lib.ERR_WORKSPACE
 
 
 def test_decode_plan_and_workspace_size(lib):
@@ -129,6 +138,9 @@ def test_decode_plan_and_workspace_size(lib):
     for L in (16384, 32768, 65536):
         assert lib.gqa_attn_decode_plan(1, L, 32, 8, 128, ctypes.byref(chunk), ctypes.byref(nsplit)) == 0
         assert nsplit.value * 8 == 256, (L, chunk.value, nsplit.value)
+    # the library's own split stays within 2^18 splits up to L = 2^30
+    assert lib.gqa_attn_decode_plan(1, 1 << 30, 32, 8, 128, ctypes.byref(chunk), ctypes.byref(nsplit)) == 0
+    assert nsplit.value <= 1 << 18
     assert lib.gqa_attn_decode_plan(1, 100, 32, 8, 128, None, None) == 0
     assert lib.gqa_attn_decode_plan(0, 100, 32, 8, 128, None, None) == _lib.ERR_DIM
 
