@@ -19,7 +19,7 @@ from . import _lib
 from ._lib import GqaAttnError  # noqa: F401
 
 __all__ = [
-    "prefill", "decode", "decode_plan", "decode_workspace_bytes", "decode_partials",
+    "prefill", "prefill_plan", "decode", "decode_plan", "decode_workspace_bytes", "decode_partials",
     "decode_combine", "default_scale", "release", "version", "GqaAttnError",
 ]
 
@@ -125,6 +125,15 @@ def decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, lens: to
                                 _stream_ptr(q))
     _lib.check(rc, "gqa_attn_decode_ws")
     return out
+
+
+def prefill_plan(B: int, S: int, Hq: int, Hkv: int, D: int = D_SUPPORTED):
+    """(waves per workgroup, workgroups) the library launches for this prefill shape."""
+    waves = ctypes.c_int(0)
+    wgs = ctypes.c_int(0)
+    rc = _lib.get().gqa_attn_prefill_plan(B, S, Hq, Hkv, D, ctypes.byref(waves), ctypes.byref(wgs))
+    _lib.check(rc, "gqa_attn_prefill_plan")
+    return waves.value, wgs.value
 
 
 def decode_plan(B: int, L: int, Hq: int, Hkv: int, D: int = D_SUPPORTED):

@@ -206,31 +206,48 @@ int gqa_attn_probe_mfma_bf16(int rounds, uint32_t seed, int workgroups,
   return GQA_ATTN_OK;
 }
 
-int gqa_attn_prefill(const void* q, const void* k, const void* v, void* out,
-                     int B, int S, int Hq, int Hkv, int D, float scale, int causal,
-                     void* stream) {
-  if (!q || !k || !v || !out) return GQA_ATTN_ERR_NULL;
+// Shape checks and launch plan of a prefill (everything but the pointers).
+int plan_prefill(int B, int S, int Hq, int Hkv, int D, float scale, gqa::PrefillArgs* a) {
   if (B < 1 || S < 1) return GQA_ATTN_ERR_DIM;
   int e = check_heads(Hq, Hkv, D, scale);
   if (e) return e;
   if (elems4(B, S, Hq) < 0) return GQA_ATTN_ERR_DIM;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ATTN_ERR_UNSUPPORTED;
+  a->B = B; a->S = S; a->Hq = Hq; a->Hkv = Hkv; a->G = Hq / Hkv;
+  a->nrb = (S + 31) / 32;
+  const long long units = (long long)a->G * a->nrb;
+  a->nw = gqa::prefill_waves(B, S, Hkv, a->G);
+  const long long wgs = (units + a->nw - 1) / a->nw;
+  const long long grid = wgs * (long long)B * Hkv;
+  if (grid > 0x7fffffffLL) return GQA_ATTN_ERR_DIM;
+  a->wgs_per_slot = (int)wgs;
+  a->nslots = B * Hkv;
+  a->c = (float)((double)scale * kLog2e);
+  return 0;
+}
+
+int gqa_attn_prefill(const void* q, const void* k, const void* v, void* out,
+                     int B, int S, int Hq, int Hkv, int D, float scale, int causal,
+                     void* stream) {
+  if (!q || !k || !v || !out) return GQA_ATTN_ERR_NULL;
   gqa::PrefillArgs a;
+  int e = plan_prefill(B, S, Hq, Hkv, D, scale, &a);
+  if (e) return e;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ATTN_ERR_UNSUPPORTED;
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.out = (uint16_t*)out;
-  a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
-  a.nrb = (S + 31) / 32;
-  const long long units = (long long)a.G * a.nrb;
-  const long long wgs = (units + 3) / 4;
-  const long long grid = wgs * (long long)B * Hkv;
-  if (grid > 0x7fffffffLL) return GQA_ATTN_ERR_DIM;
-  a.wgs_per_slot = (int)wgs;
-  a.nslots = B * Hkv;
-  a.c = (float)((double)scale * kLog2e);
   e = gqa::launch_prefill(a, causal != 0, (hipStream_t)stream);
   if (e != 0) return hip_fail("prefill launch", e);
+  return GQA_ATTN_OK;
+}
+
+int gqa_attn_prefill_plan(int B, int S, int Hq, int Hkv, int D, int* waves, int* workgroups) {
+  gqa::PrefillArgs a;
+  const int e = plan_prefill(B, S, Hq, Hkv, D, 1.0f, &a);
+  if (e) return e;
+  if (waves) *waves = a.nw;
+  if (workgroups) *workgroups = a.wgs_per_slot * a.nslots;
   return GQA_ATTN_OK;
 }
 

@@ -14,7 +14,8 @@ struct PrefillArgs {
   uint16_t* out;         // [B, S, Hq, D]
   int B, S, Hq, Hkv, G;  // G = Hq / Hkv
   int nrb;               // 32-row query blocks per sequence: ceil(S / 32)
-  int wgs_per_slot;      // workgroups per (b, kv head): ceil(G * nrb / 4)
+  int nw;                // waves per workgroup (4 or 8; prefill_waves)
+  int wgs_per_slot;      // workgroups per (b, kv head): ceil(G * nrb / nw)
   int nslots;            // B * Hkv
   float c;               // scale * log2(e)
 };
@@ -43,6 +44,8 @@ struct CombineArgs {
 };
 
 // Each returns a hipError_t value (0 = success) from the launch.
+// Waves per prefill workgroup the library uses for this shape (4 or 8).
+int prefill_waves(int B, int S, int Hkv, int G);
 int launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
 // fused = true: split, then merge in the last-arriving workgroup, writing `out`.
 // fused = false: only the per-chunk partials (o_part, lse).

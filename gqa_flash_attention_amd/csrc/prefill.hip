@@ -14,7 +14,16 @@
 //    logits, on the native v_exp_f32.
 //
 // Work decomposition. One wave owns 32 query rows of one head and keeps, per lane, one
-// query row (lane % 32) and half of the keys of every tile (lane / 32). Scores are
+// query row (lane % 32) and half of the keys of every tile (lane / 32). A workgroup is
+// NW = 4 waves (one 32-row block of each head of a KV group; two workgroups per CU) or
+// NW = 8 waves (two row blocks; one workgroup per CU). K/V tiles go through a ring of
+// 2P stages in LDS, P = NW / 4, and are published P at a time: wait for this wave's
+// copies, one barrier, then the copies of the next P tiles into the stages the barrier
+// has freed. The 8-wave form copies each tile once for 256 query rows instead of 128
+// and meets a barrier every other tile; with a single workgroup per CU a barrier idles
+// the whole CU, so halving them is what makes it pay (3-4% at 16K-32K keys on MI355X).
+// It needs at least 4 workgroups per CU to balance the causal triangle, so short
+// prompts keep the 4-wave form. Scores are
 // computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K from LDS is the A
 // operand, the wave's Q rows stay in registers as the B operand. In that layout each
 // lane's 32 scores of a 64-key tile belong to its own query row, so the row max needs
@@ -33,17 +42,13 @@ namespace gqa {
 
 constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 units (p <= 2^8)
 
-template <bool CAUSAL, bool POS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <bool CAUSAL, bool POS, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[kTileBytes];
-  GQA_LDS uint8_t* const K0 = (GQA_LDS uint8_t*)lds_k0;
-  GQA_LDS uint8_t* const V0 = (GQA_LDS uint8_t*)lds_v0;
-  GQA_LDS uint8_t* const K1 = (GQA_LDS uint8_t*)lds_k1;
-  GQA_LDS uint8_t* const V1 = (GQA_LDS uint8_t*)lds_v1;
+  static_assert(NW == 4 || NW == 8, "waves per workgroup");
+  constexpr int P = NW / 4;      // tiles published per barrier
+  constexpr int NST = 2 * P;     // ring stages, one K tile and one V tile each
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv[NST][2][kTileBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -61,13 +66,13 @@ void prefill_kernel(PrefillArgs a) {
   const int b = slot / a.Hkv;
   const int g = slot % a.Hkv;
   const int nunits = a.G * a.nrb;
-  const int unit = 4 * wg + wave;
+  const int unit = NW * wg + wave;
   const bool active = unit < nunits;
   const int rb = active ? unit / a.G : 0;
   const int head = g * a.G + (active ? unit % a.G : 0);
   const int q0 = rb * 32;
 
-  const int last_unit = min(4 * wg + 3, nunits - 1);
+  const int last_unit = min(NW * wg + NW - 1, nunits - 1);
   const int kv_end = CAUSAL ? min(a.S, (last_unit / a.G) * 32 + 32) : a.S;
   const int nt = (kv_end + kTileRows - 1) / kTileRows;
   const int own_end = CAUSAL ? min(a.S, q0 + 32) : a.S;
@@ -77,7 +82,7 @@ void prefill_kernel(PrefillArgs a) {
   const uint16_t* kbase = a.k + ((size_t)b * a.S * a.Hkv + g) * kD;
   const uint16_t* vbase = a.v + ((size_t)b * a.S * a.Hkv + g) * kD;
 
-  TileCopy<4> copy;
+  TileCopy<NW> copy;
   copy.init(kv_stride, wave, lane);
   // Copies of tile t (K then V): the per-lane offsets for a full tile, the clamped
   // per-row path for the ragged last tile.
@@ -86,13 +91,15 @@ void prefill_kernel(PrefillArgs a) {
     if (kv_end - r0 >= kTileRows) {
       copy.issue_full(kd, vd, kbase + (size_t)r0 * kv_stride, vbase + (size_t)r0 * kv_stride, wave);
     } else {
-      stage_tile<4, false>(kd, kbase + (size_t)r0 * kv_stride, kv_stride, kv_end - r0, wave, lane);
-      stage_tile<4, true>(vd, vbase + (size_t)r0 * kv_stride, kv_stride, kv_end - r0, wave, lane);
+      stage_tile<NW, false>(kd, kbase + (size_t)r0 * kv_stride, kv_stride, kv_end - r0, wave, lane);
+      stage_tile<NW, true>(vd, vbase + (size_t)r0 * kv_stride, kv_stride, kv_end - r0, wave, lane);
     }
   };
 
+  auto kbuf = [&](int st) { return (GQA_LDS uint8_t*)lds_kv[st][0]; };
+  auto vbuf = [&](int st) { return (GQA_LDS uint8_t*)lds_kv[st][1]; };
   // Prologue: start tile 0, then fetch this wave's Q rows (B operand, 8 k-steps of 16 d).
-  issue_tile(0, K0, V0);
+  issue_tile(0, kbuf(0), vbuf(0));
   bf16x8 qreg[8];
   {
     const int qrow = min(q0 + qi, a.S - 1);
@@ -101,8 +108,11 @@ void prefill_kernel(PrefillArgs a) {
     for (int ks = 0; ks < 8; ++ks) qreg[ks] = *(const bf16x8*)(qp + 16 * ks);
   }
   // Q and tile 0 have landed. Waiting here also tells the compiler that no load of its
-  // own is outstanding inside the loop, so it adds no waits there.
+  // own is outstanding inside the loop, so it adds no waits there. Then tiles 1..P-1.
   wait_vmcnt<0>();
+#pragma unroll
+  for (int t = 1; t < P; ++t)
+    if (t < nt) issue_tile(t, kbuf(t), vbuf(t));
 
   const float c = a.c;
   float m_run = -INFINITY;
@@ -111,25 +121,24 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) oacc[mb] = f32x16{};
 
-  // One key tile. BUF selects the LDS buffers at compile time, so every LDS access
-  // names one __shared__ array and the copies into the other buffer are known not to
-  // alias the reads of this one.
+  // One key tile. BUF = t % NST selects the ring stage at compile time.
   auto step = [&](int t, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
-    GQA_LDS uint8_t* const kt = BUF ? K1 : K0;
-    GQA_LDS uint8_t* const vt = BUF ? V1 : V0;
-    GQA_LDS uint8_t* const kn = BUF ? K0 : K1;
-    GQA_LDS uint8_t* const vn = BUF ? V0 : V1;
-    // Every wave is done with the buffers of tile t-1 (kn/vn) before they are refilled:
-    // its LDS reads of them fed MFMAs that have issued, so they have completed.
-    tile_barrier();
-    if (t + 1 < nt) {
-      issue_tile(t + 1, kn, vn);
-      wait_vmcnt<8>();   // this wave's copies of tile t have landed (8 of t+1 may remain)
-    } else {
+    GQA_LDS uint8_t* const kt = kbuf(BUF);
+    GQA_LDS uint8_t* const vt = vbuf(BUF);
+    // At t = 0 mod P this wave's copies of tiles t .. t+P-1 (the only ones in flight)
+    // land; after the barrier every wave's have, and every wave is done with tiles
+    // t-P .. t-1: their LDS reads fed MFMAs that have issued, so they have completed.
+    // Their stages then take tiles t+P .. t+2P-1.
+    if (BUF % P == 0) {
       wait_vmcnt<0>();
+      tile_barrier();
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int nx = (BUF + P + i) % NST;
+        if (t + P + i < nt) issue_tile(t + P + i, kbuf(nx), vbuf(nx));
+      }
     }
-    tile_barrier();      // ... and so have every other wave's
     if (!active || t >= own_nt) return;
 
     // S^T[key][query] for the tile's 64 keys, two 32-key blocks. The K operand reads run
@@ -232,9 +241,11 @@ void prefill_kernel(PrefillArgs a) {
     __builtin_amdgcn_s_setprio(0);
   };
 
-  for (int t = 0; t < nt; t += 2) {
+  for (int t = 0; t < nt; t += NST) {
     step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < nt) step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 1 < nt) step(t + 1, std::integral_constant<int, 1 % NST>{});
+    if (NST > 2 && t + 2 < nt) step(t + 2, std::integral_constant<int, 2 % NST>{});
+    if (NST > 3 && t + 3 < nt) step(t + 3, std::integral_constant<int, 3 % NST>{});
   }
 
   // Epilogue: the two halves of the wave hold disjoint keys of the same rows.
@@ -259,17 +270,31 @@ void prefill_kernel(PrefillArgs a) {
   }
 }
 
-int launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream) {
+int prefill_waves(int B, int S, int Hkv, int G) {
+  // 8 waves once their grid holds at least 4 workgroups per CU (B = 1, 32 query and 8 KV
+  // heads: S > 8128).
+  const long long units = (long long)G * ((S + 31) / 32);
+  const long long wgs8 = (long long)B * Hkv * ((units + 7) / 8);
+  return wgs8 >= 4 * 256 ? 8 : 4;
+}
+
+template <int NW>
+static void launch_prefill_nw(const PrefillArgs& a, bool causal, hipStream_t stream) {
   const dim3 grid((unsigned)((size_t)a.nslots * a.wgs_per_slot));
-  const dim3 block(256);
+  const dim3 block(64 * NW);
   const bool pos = a.c > 0.f;
   if (causal) {
-    if (pos) hipLaunchKernelGGL((prefill_kernel<true, true>), grid, block, 0, stream, a);
-    else     hipLaunchKernelGGL((prefill_kernel<true, false>), grid, block, 0, stream, a);
+    if (pos) hipLaunchKernelGGL((prefill_kernel<true, true, NW>), grid, block, 0, stream, a);
+    else     hipLaunchKernelGGL((prefill_kernel<true, false, NW>), grid, block, 0, stream, a);
   } else {
-    if (pos) hipLaunchKernelGGL((prefill_kernel<false, true>), grid, block, 0, stream, a);
-    else     hipLaunchKernelGGL((prefill_kernel<false, false>), grid, block, 0, stream, a);
+    if (pos) hipLaunchKernelGGL((prefill_kernel<false, true, NW>), grid, block, 0, stream, a);
+    else     hipLaunchKernelGGL((prefill_kernel<false, false, NW>), grid, block, 0, stream, a);
   }
+}
+
+int launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream) {
+  if (a.nw == 8) launch_prefill_nw<8>(a, causal, stream);
+  else           launch_prefill_nw<4>(a, causal, stream);
   return (int)hipGetLastError();
 }
 

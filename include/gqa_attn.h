@@ -67,6 +67,16 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, void* out,
                      void* stream);
 
 /*
+ * The launch gqa_attn_prefill uses for this shape. Each wave owns 32 query rows
+ * of one head; *waves (4 or 8) is the number of waves per workgroup, all serving
+ * one KV head, and *workgroups the size of the grid. The 8-wave form is taken
+ * once its grid holds at least 4 workgroups per CU (for B = 1 with 32 query and
+ * 8 KV heads: S > 8128). Either
+ * output may be NULL. Returns the same shape errors as gqa_attn_prefill.
+ */
+int gqa_attn_prefill_plan(int B, int S, int Hq, int Hkv, int D, int* waves, int* workgroups);
+
+/*
  * One-token decode against a KV cache, split along the cache.
  *   q, out         : [B, Hq, D]  bf16
  *   kcache, vcache : [B, L, Hkv, D] bf16; L is the capacity (the row stride).

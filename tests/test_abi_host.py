@@ -145,6 +145,24 @@ def test_decode_plan_and_workspace_size(lib):
     assert lib.gqa_attn_decode_plan(0, 100, 32, 8, 128, None, None) == _lib.ERR_DIM
 
 
+def test_prefill_plan(lib):
+    waves = ctypes.c_int(0)
+    wgs = ctypes.c_int(0)
+    # batch 1, Llama-3-8B heads: 4-wave workgroups (2 per CU) below 8K keys, 8 from there
+    for S, want in ((1, 4), (512, 4), (4096, 4), (8128, 4), (8129, 8), (8192, 8), (32768, 8)):
+        assert lib.gqa_attn_prefill_plan(1, S, 32, 8, 128, ctypes.byref(waves), ctypes.byref(wgs)) == 0
+        assert waves.value == want, S
+        units = 4 * -(-S // 32)
+        assert wgs.value == 8 * -(-units // want)
+    # a batch reaches 4 workgroups per CU sooner
+    assert lib.gqa_attn_prefill_plan(8, 1000, 32, 8, 128, ctypes.byref(waves), None) == 0
+    assert waves.value == 8
+    assert lib.gqa_attn_prefill_plan(1, 100, 32, 8, 128, None, None) == 0
+    assert lib.gqa_attn_prefill_plan(0, 100, 32, 8, 128, None, None) == _lib.ERR_DIM
+    assert lib.gqa_attn_prefill_plan(1, 100, 32, 8, 64, None, None) == _lib.ERR_UNSUPPORTED
+    assert lib.gqa_attn_prefill_plan(1, 100, 30, 8, 128, None, None) == _lib.ERR_DIM
+
+
 def test_release_without_any_workspace_is_harmless(lib):
     lib.gqa_attn_release()
 
