@@ -367,7 +367,10 @@ def main_line(args):
 
 def sweep(path, steps, warmup):
     """Every prefill and decode size of the workload, each timed on its own (events per call).
-    Decode caches are rotated through >= 1 GB of distinct copies so the MALL holds none."""
+    Each size first runs ~0.2 s of calls (the board's power management needs that long to
+    settle the clock; a fixed count of short calls would time a ramping clock), then at least
+    `steps` timed calls and ~50 ms of them. Decode caches are rotated through >= 1 GB of
+    distinct copies so the MALL holds none."""
     import torch
     import gqa_flash_attention_amd as gqa
     from gqa_inputs import decode_inputs, prefill_inputs, seed_base
@@ -384,12 +387,26 @@ def sweep(path, steps, warmup):
         torch.cuda.synchronize()
         return sorted(a.elapsed_time(b) for a, b in evs)
 
+    def settle(fn, n0):
+        """Run ~0.2 s of calls after n0 warm-up calls; return how many calls make ~50 ms."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n0):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per = max(e0.elapsed_time(e1) / max(n0, 1), 1e-3)     # ms per call
+        for i in range(min(20000, int(200.0 / per))):
+            fn(i)
+        torch.cuda.synchronize()
+        return min(4000, int(50.0 / per))
+
     for S in (512, 2048, 4096, 8192, 16384, 32768):
         q, k, v = [x.to(dev) for x in prefill_inputs(1, S, base=seed_base(2, 0))]
         out = torch.empty_like(q)
-        for _ in range(warmup):
-            gqa.prefill(q, k, v, out=out)
-        ms = timed(lambda i: gqa.prefill(q, k, v, out=out), steps)
+        call = lambda i: gqa.prefill(q, k, v, out=out)
+        n = settle(call, max(warmup, 3))
+        ms = timed(call, max(steps, n))
         med = ms[len(ms) // 2]
         r = {"mode": "prefill", "S": S, "ms_median": med, "ms_min": ms[0],
              "tflops": prefill_flops(S) / (med * 1e-3) / 1e12}
@@ -405,9 +422,9 @@ def sweep(path, steps, warmup):
         kcs = [kc.to(dev) for _ in range(ncopies)]
         vcs = [vc.to(dev) for _ in range(ncopies)]
         out = torch.empty_like(qd)
-        for i in range(warmup):
-            gqa.decode(qd, kcs[i % ncopies], vcs[i % ncopies], lens, out=out)
-        ms = timed(lambda i: gqa.decode(qd, kcs[i % ncopies], vcs[i % ncopies], lens, out=out), max(steps, 2 * ncopies))
+        call = lambda i: gqa.decode(qd, kcs[i % ncopies], vcs[i % ncopies], lens, out=out)
+        n = settle(call, max(warmup, ncopies))
+        ms = timed(call, max(steps, 2 * ncopies, n))
         med = ms[len(ms) // 2]
         r = {"mode": "decode", "L": L, "ms_median": med, "ms_min": ms[0], "copies_rotated": ncopies,
              "gbs": decode_bytes(L) / (med * 1e-3) / 1e9}
