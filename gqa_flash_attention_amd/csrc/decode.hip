@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         lds_dma16(qrow + (size_t)hh * kD + 8 * (lane & 15), (GQA_LDS uint8_t*)lds_q + i * 1024);
       }
     }
-    TileCopy<kDecWaves> copy;
+    TileCopy<kDecWaves, true> copy;   // the cache is read once: non-temporal copies
     copy.init(kv_stride, wave, lane);
     // Copies of the t-th streamed tile (K then V): per-lane offsets for a full tile, the
     // clamped per-row path for the ragged last tile.
@@ -152,8 +152,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       if (len - r0 >= kTileRows) {
         copy.issue_full(st, st + kTileBytes, kbase + off, vbase + off, wave);
       } else {
-        stage_tile<kDecWaves, false>(st, kbase + off, kv_stride, len - r0, wave, lane);
-        stage_tile<kDecWaves, true>(st + kTileBytes, vbase + off, kv_stride, len - r0, wave, lane);
+        stage_tile<kDecWaves, false, true>(st, kbase + off, kv_stride, len - r0, wave, lane);
+        stage_tile<kDecWaves, true, true>(st + kTileBytes, vbase + off, kv_stride, len - r0, wave, lane);
       }
     };
     for (int t = 0; t < NSTAGE - 1; ++t)
