@@ -5,9 +5,10 @@
 // register-resident matrix-instruction loop per data type, each reported with the clock
 // it ran at ("Return schemas": value, units, method, clock). These are the two probes the
 // attention kernels need on gfx950:
-//  - hbm_read: every byte of a caller buffer read once with 16-byte loads, the decode
-//    kernel's access width. On a buffer several times the 256 MB MALL this is the cold
-//    HBM read rate a decode can reach.
+//  - hbm_read: every byte of a caller buffer read once with 16-byte non-temporal loads,
+//    the decode kernel's access width and cache policy (on MI355X non-temporal reads of
+//    a 2 GiB buffer run ~6.0 TB/s against ~5.4 for plain ones). On a buffer several times
+//    the 256 MB MALL this is the cold HBM read rate a decode can reach.
 //  - mfma_bf16: v_mfma_f32_32x32x16_bf16 from registers, 2 waves per SIMD on every CU, 8
 //    independent accumulators per wave, the A and B operands drawn from 8 registers of
 //    random bf16 each in a rotating pairing, so that consecutive instructions see new
@@ -41,10 +42,13 @@ __global__ __launch_bounds__(256) void probe_hbm_read_kernel(const u32x4* src, s
   size_t i = tid;
   // four independent 16-byte loads in flight per lane
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
     acc ^= a ^ b ^ c ^ d;
   }
-  for (; i < n16; i += stride) acc ^= src[i];
+  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
   sink[tid] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 

@@ -166,7 +166,8 @@ int gqa_attn_decode_combine(const void* ws, size_t ws_bytes, void* out,
  * limits of the two attention kernels. The caller times each call (for example
  * with events on `stream`); neither allocates.
  *
- * Cold HBM read rate: every byte of buf is read once with 16-byte loads.
+ * Cold HBM read rate: every byte of buf is read once with 16-byte non-temporal
+ * loads (the decode kernel's width and cache policy).
  *   buf        : device, 16-byte aligned; bytes > 0 and a multiple of 16. A buffer
  *                several times the 256 MB MALL measures HBM, not the cache.
  *   workgroups : 1..65535 workgroups of 256 lanes (4096 suits MI355X).
