@@ -85,11 +85,15 @@ int gqa_attn_prefill_plan(int B, int S, int Hq, int Hkv, int D, int* waves, int*
  *                    on the host. lens[b] = 0 gives a zero output row. Slots at
  *                    or past lens[b] are never read, whatever they hold.
  * Implements the decode mode ("Result": decode generates one token from a KV
- * cache of a given length). The cache is cut into chunks that run in parallel
- * on all CUs and are then merged by log-sum-exp ("What helped most", item 1).
- * Each chunk's K/V rows are read once for all query heads of their group
- * (item 2). The merge happens in the same kernel launch (item 5, one fewer
- * launch): the last workgroup to finish a (sequence, KV head) merges it.
+ * cache of a given length). The cache is cut into nsplit splits that run in
+ * parallel on all CUs and are then merged by log-sum-exp ("What helped most",
+ * item 1); split s holds the 64-key tiles s, s + nsplit, s + 2 nsplit, ... of
+ * the sequence, so the splits of a head read one contiguous stretch of the
+ * cache at a time and a short sequence still spreads over all of them. Each
+ * split's K/V rows are read once, with non-temporal loads, for all query heads
+ * of their group (item 2). The merge happens in the same kernel launch (item 5,
+ * one fewer launch): the last workgroup to finish a (sequence, KV head) merges
+ * it.
  * The split partials live in a library-owned workspace, cached per (device,
  * stream) and grown on demand: one hipMalloc (and a clear of the new buffer)
  * the first time a larger size is needed, none afterwards. Concurrent streams
@@ -122,10 +126,11 @@ size_t gqa_attn_decode_workspace_bytes(int B, int L, int Hq, int Hkv, int D, int
 
 /*
  * Decode with a caller-owned workspace and an explicit split size. Same
- * semantics as gqa_attn_decode. chunk = 0 takes the library's choice;
- * otherwise chunk must be a positive multiple of 64 with ceil(L / chunk) at
- * most 2^18. ws must be 16-byte
- * aligned and hold at least gqa_attn_decode_workspace_bytes(..., chunk) bytes.
+ * semantics as gqa_attn_decode, with nsplit = ceil(L / chunk) splits of about
+ * chunk keys each. chunk = 0 takes the library's choice; otherwise chunk must
+ * be a positive multiple of 64 with ceil(L / chunk) at most 2^18. ws must be
+ * 16-byte aligned and hold at least gqa_attn_decode_workspace_bytes(..., chunk)
+ * bytes.
  * The counters part of ws (its first max(4096, B*Hq) int32) must hold zeros
  * before the call: allocate the buffer zeroed; each completed call leaves the
  * counters zero again. Two calls in flight on the same workspace race.
@@ -137,8 +142,10 @@ int gqa_attn_decode_ws(const void* q, const void* kcache, const void* vcache,
                        int chunk, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * The first half of a decode on its own: per-split partial results.
- * Writes, for every (b, h, split s) with chunk keys per split:
+ * The first half of a decode on its own: per-split partial results. Here split
+ * s is the contiguous chunk of cache slots [s*chunk, (s+1)*chunk), clipped to
+ * lens[b] (the fused entry points above assign keys to splits differently; their
+ * partials never leave the library). Writes, for every (b, h, split s):
  *   o_part[b][h][s][:] (fp32, the chunk's softmax-weighted mean of V) and
  *   lse[b][h][s]       (fp32, log2 of sum_j 2^(x_j * log2(e)) over the chunk,
  *                       i.e. the chunk's log-sum-exp in base-2 units;
