@@ -373,7 +373,7 @@ def sweep(path, steps, warmup):
     distinct copies so the MALL holds none."""
     import torch
     import gqa_flash_attention_amd as gqa
-    from gqa_inputs import decode_inputs, prefill_inputs, seed_base
+    from gqa_inputs import decode_inputs, prefill_inputs, random_lens, randn_bf16_device, seed_base
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     rows = []
@@ -401,7 +401,8 @@ def sweep(path, steps, warmup):
         torch.cuda.synchronize()
         return min(4000, int(50.0 / per))
 
-    for S in (512, 2048, 4096, 8192, 16384, 32768):
+    # the workload's sizes, then its ragged prefill lengths
+    for S in (512, 2048, 4096, 8192, 16384, 32768, 1, 127, 3000):
         q, k, v = [x.to(dev) for x in prefill_inputs(1, S, base=seed_base(2, 0))]
         out = torch.empty_like(q)
         call = lambda i: gqa.prefill(q, k, v, out=out)
@@ -433,6 +434,26 @@ def sweep(path, steps, warmup):
         rows.append(r)
         del kcs, vcs
         torch.cuda.empty_cache()
+    # the ragged batch: B = 16, capacity 50001, lengths U[1, 50001] (the parity tests' seed);
+    # each cache copy is 3.3 GB, so every call reads cold from HBM
+    B, L = 16, 50001
+    lens = random_lens(B, 1, L, seed=seed_base(4, 3) + 3).to(dev)
+    qd = randn_bf16_device((B, HQ, D), seed_base(4, 3), dev)
+    kcs = [randn_bf16_device((B, L, HKV, D), seed_base(4, 3) + 10 + i, dev) for i in range(2)]
+    vcs = [randn_bf16_device((B, L, HKV, D), seed_base(4, 3) + 20 + i, dev) for i in range(2)]
+    out = torch.empty_like(qd)
+    call = lambda i: gqa.decode(qd, kcs[i % 2], vcs[i % 2], lens, out=out)
+    n = settle(call, max(warmup, 2))
+    ms = timed(call, max(steps, n))
+    med = ms[len(ms) // 2]
+    total = int(lens.sum().item())
+    r = {"mode": "decode_ragged", "B": B, "L": L, "sum_lens": total, "ms_median": med, "ms_min": ms[0],
+         "gbs": decode_bytes(total, B) / (med * 1e-3) / 1e9}
+    r["frac_of_peak"] = r["gbs"] / PEAK_HBM_GBS
+    print(json.dumps(r), flush=True)
+    rows.append(r)
+    del kcs, vcs
+    torch.cuda.empty_cache()
     with open(path, "w") as f:
         for r in rows:
             f.write(json.dumps(r) + "\n")
