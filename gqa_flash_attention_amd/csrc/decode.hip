@@ -3,15 +3,15 @@
 // Implements the decode mode of the chowfi/kernels README ("Result": generate one token
 // from a KV cache of a given length) with the decode ideas of its "What helped most"
 // section, redone for CDNA4:
-//  - item 1 (split-KV): the cache is cut into chunks; one workgroup per (chunk, KV head,
-//    sequence) spreads a single query over all 256 CUs, and the chunk results are merged
+//  - item 1 (split-KV): the cache is cut into splits; one workgroup per (split, KV head,
+//    sequence) spreads a single query over all 256 CUs, and the split results are merged
 //    by log-sum-exp;
-//  - item 2 (GQA packing): a workgroup reads each K/V row of its chunk once and scores it
+//  - item 2 (GQA packing): a workgroup reads each K/V row of its split once and scores it
 //    against all query heads of the group (up to 16 per pass) with one matrix-core
 //    instruction;
 //  - item 5 (one fewer launch in short decodes): the merge is fused into the same kernel.
 //    The last workgroup of a (sequence, KV head) to finish merges the partials of all
-//    chunks; with a single chunk the result is written directly.
+//    splits; with a single split the result is written directly.
 //
 // Streaming. A workgroup walks its split's keys in 64-key tiles through an LDS ring of
 // NSTAGE stages (K 16 KB + V 16 KB each). Tiles are copied with global_load_lds_dwordx4
@@ -34,7 +34,7 @@
 // the query heads in registers as B; an online softmax in base 2 per head; then
 // O^T (d x heads) += V^T P^T with v_mfma_f32_16x16x16_bf16, whose B operand is the score
 // accumulator layout as is and whose A operand (V^T) comes from ds_read_b64_tr_b16.
-// The four waves merge their (max, sum, O) through LDS at the end of the chunk.
+// The four waves merge their (max, sum, O) through LDS at the end of the split.
 #include "gqa_device.hpp"
 #include "gqa_internal.hpp"
 
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
     }
   } else {
-    // Nothing to attend in this chunk: weight zero in the merge.
+    // Nothing to attend in this split: weight zero in the merge.
     if (threadIdx.x < nheads) publish(lse_out + (size_t)threadIdx.x * a.nsplit, -INFINITY);
     if (FUSE && a.nsplit == 1) {
       for (int idx = threadIdx.x; idx < nheads * kD; idx += 256) a.out[head0 * kD + idx] = 0;
@@ -283,9 +283,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   if (!FUSE || a.nsplit == 1) return;
 
-  // Count this chunk. The partial was written with device-coherent stores, and the
+  // Count this split. The partial was written with device-coherent stores, and the
   // barrier below waits for them to complete (vmcnt(0)) before the count, so when the
-  // last workgroup's count returns, every chunk's partial is in memory. That workgroup
+  // last workgroup's count returns, every split's partial is in memory. That workgroup
   // merges them, reading with device-coherent loads (which cannot hit a stale line in
   // its XCD's L2, so no cache-wide invalidation is needed), and afterwards resets the
   // counter for the next call. No workgroup ever waits for another.
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   if (!s_last) return;
 
   // out[h, d] = sum_s 2^(lse_s - M) o_s[d] / sum_s 2^(lse_s - M). Thread -> (head, 4
-  // consecutive d) column and a share of the chunks, kBatch chunks per round of loads;
+  // consecutive d) column and a share of the splits, kBatch splits per round of loads;
   // within a round one maximum and independent weights, across rounds a rescale.
   constexpr int kBatch = 16;
   const int ncols = nheads * (kD / 4);
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         float mb = m;
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-          // past the last chunk, or an empty chunk (lse = -inf, o_part row never written)
+          // past the last split, or an empty split (lse = -inf, o_part row never written)
           if (s0 + j * nparts >= a.nsplit || lv[j] == -INFINITY) {
             lv[j] = -INFINITY;
             ov[j] = f32x4{};
@@ -388,9 +388,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Stand-alone merge of per-chunk partials (the second half of a decode on its own):
+// Stand-alone merge of per-split partials (the second half of a decode on its own):
 // out[b, h, :] = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max finite lse_s.
-// Grid (D/32, Hq, B); 256 threads = 8 groups of 32 lanes; lane -> d, group -> chunks.
+// Grid (D/32, Hq, B); 256 threads = 8 groups of 32 lanes; lane -> d, group -> splits.
 __global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs a) {
   __shared__ float red_m[8];
   __shared__ float red_num[8][32];
