@@ -434,6 +434,40 @@ def sweep(path, steps, warmup):
         rows.append(r)
         del kcs, vcs
         torch.cuda.empty_cache()
+    # decodes replayed from one HIP graph (16 calls on rotated caches, caller workspace):
+    # the per-call cost of a decode loop once the launch gaps are gone
+    for L in (2048, 16384, 65536):
+        per = L * HKV * D * 2 * 2
+        ncopies = max(2, min(16, -(-(1 << 30) // per)))
+        qd, kc, vc, lens = decode_inputs(1, L, base=seed_base(1, 0))
+        qd, lens = qd.to(dev), lens.to(dev)
+        kcs = [kc.to(dev) for _ in range(ncopies)]
+        vcs = [vc.to(dev) for _ in range(ncopies)]
+        ws = torch.zeros(gqa.decode_workspace_bytes(1, L, HQ, HKV, D), dtype=torch.uint8, device=dev)
+        outs = [torch.empty_like(qd) for _ in range(16)]
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for i in range(16):
+                gqa.decode(qd, kcs[i % ncopies], vcs[i % ncopies], lens, out=outs[i], workspace=ws)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(16):
+                gqa.decode(qd, kcs[i % ncopies], vcs[i % ncopies], lens, out=outs[i], workspace=ws)
+        torch.cuda.synchronize()
+        call = lambda i: graph.replay()
+        n = settle(call, 3)
+        ms = timed(call, max(steps, n))
+        med = ms[len(ms) // 2] / 16
+        r = {"mode": "decode_graph", "L": L, "calls_per_replay": 16, "ms_median_per_call": med,
+             "gbs": decode_bytes(L) / (med * 1e-3) / 1e9}
+        r["frac_of_peak"] = r["gbs"] / PEAK_HBM_GBS
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+        del graph, kcs, vcs, ws, outs
+        torch.cuda.empty_cache()
     # the ragged batch: B = 16, capacity 50001, lengths U[1, 50001] (the parity tests' seed);
     # each cache copy is 3.3 GB, so every call reads cold from HBM
     B, L = 16, 50001
