@@ -35,6 +35,17 @@ def _stream_ptr(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _check_workspace(ws, device) -> None:
+    """A caller-owned workspace: a contiguous uint8 tensor on the device of the call (the
+    library checks its size and 16-byte alignment)."""
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    if not ws.is_cuda or ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, expected {device}")
+
+
 def _check_bf16(name: str, t: torch.Tensor, ndim: int, device=None) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -68,8 +79,9 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Tr
             raise ValueError("out must have q's shape")
     if scale is None:
         scale = default_scale(D)
-    rc = _lib.get().gqa_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                     B, S, Hq, Hkv, D, float(scale), 1 if causal else 0, _stream_ptr(q))
+    with torch.cuda.device(q.device):
+        rc = _lib.get().gqa_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         B, S, Hq, Hkv, D, float(scale), 1 if causal else 0, _stream_ptr(q))
     _lib.check(rc, "gqa_attn_prefill")
     return out
 
@@ -109,20 +121,22 @@ def decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, lens: to
     if scale is None:
         scale = default_scale(D)
     lib = _lib.get()
-    if chunk is None and workspace is None:
-        rc = lib.gqa_attn_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), lens.data_ptr(),
-                                 out.data_ptr(), B, L, Hq, Hkv, D, float(scale), _stream_ptr(q))
-        _lib.check(rc, "gqa_attn_decode")
-        return out
-    ch = 0 if chunk is None else int(chunk)
-    need = lib.gqa_attn_decode_workspace_bytes(B, L, Hq, Hkv, D, ch)
-    if workspace is None:
-        # zeroed: the merge counters at the end of the workspace must start at zero
-        workspace = torch.zeros(max(int(need), 16), dtype=torch.uint8, device=q.device)
-    rc = lib.gqa_attn_decode_ws(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), lens.data_ptr(),
-                                out.data_ptr(), B, L, Hq, Hkv, D, float(scale), ch,
-                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                _stream_ptr(q))
+    if workspace is not None:
+        _check_workspace(workspace, q.device)
+    with torch.cuda.device(q.device):
+        if chunk is None and workspace is None:
+            rc = lib.gqa_attn_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), lens.data_ptr(),
+                                     out.data_ptr(), B, L, Hq, Hkv, D, float(scale), _stream_ptr(q))
+            _lib.check(rc, "gqa_attn_decode")
+            return out
+        ch = 0 if chunk is None else int(chunk)
+        need = lib.gqa_attn_decode_workspace_bytes(B, L, Hq, Hkv, D, ch)
+        if workspace is None:
+            # zeroed: the merge counters at the start of the workspace must start at zero
+            workspace = torch.zeros(max(int(need), 16), dtype=torch.uint8, device=q.device)
+        rc = lib.gqa_attn_decode_ws(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), lens.data_ptr(),
+                                    out.data_ptr(), B, L, Hq, Hkv, D, float(scale), ch,
+                                    workspace.data_ptr(), workspace.numel(), _stream_ptr(q))
     _lib.check(rc, "gqa_attn_decode_ws")
     return out
 
@@ -170,9 +184,10 @@ def decode_partials(q, kcache, vcache, lens, chunk: int, scale: float | None = N
     if need == 0:
         raise GqaAttnError(_lib.ERR_WORKSPACE, "gqa_attn_decode_workspace_bytes")
     ws = torch.zeros(need, dtype=torch.uint8, device=q.device)
-    rc = lib.gqa_attn_decode_partials(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), lens.data_ptr(),
-                                      B, L, Hq, Hkv, D, float(scale), int(chunk), ws.data_ptr(), need,
-                                      _stream_ptr(q))
+    with torch.cuda.device(q.device):
+        rc = lib.gqa_attn_decode_partials(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), lens.data_ptr(),
+                                          B, L, Hq, Hkv, D, float(scale), int(chunk), ws.data_ptr(), need,
+                                          _stream_ptr(q))
     _lib.check(rc, "gqa_attn_decode_partials")
     nsplit = -(-L // int(chunk))
     o_part, lse = _split_views(ws, B, Hq, nsplit, D)
@@ -182,10 +197,18 @@ def decode_partials(q, kcache, vcache, lens, chunk: int, scale: float | None = N
 def decode_combine(ws: torch.Tensor, B: int, Hq: int, nsplit: int, D: int = D_SUPPORTED,
                    out: torch.Tensor | None = None) -> torch.Tensor:
     """The merge half of a decode: workspace (as written by decode_partials) -> out [B,Hq,D] bf16."""
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda:
+        raise ValueError("ws must be a GPU tensor (the workspace decode_partials returned)")
+    _check_workspace(ws, ws.device)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=ws.device)
-    rc = _lib.get().gqa_attn_decode_combine(ws.data_ptr(), ws.numel() * ws.element_size(), out.data_ptr(),
-                                            B, Hq, D, nsplit, _stream_ptr(out))
+    else:
+        _check_bf16("out", out, 3, ws.device)
+        if tuple(out.shape) != (B, Hq, D):
+            raise ValueError(f"out must be [{B}, {Hq}, {D}]")
+    with torch.cuda.device(ws.device):
+        rc = _lib.get().gqa_attn_decode_combine(ws.data_ptr(), ws.numel(), out.data_ptr(),
+                                                B, Hq, D, nsplit, _stream_ptr(out))
     _lib.check(rc, "gqa_attn_decode_combine")
     return out
 

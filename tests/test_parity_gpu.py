@@ -297,3 +297,23 @@ def test_invalid_arguments_on_gpu_raise_cleanly():
     with pytest.raises(gqa.GqaAttnError):
         gqa.prefill(mis, kd, vd)
     torch.cuda.synchronize()
+
+
+def test_workspace_and_output_checks_in_the_binding():
+    _say("decode workspace on the host, of the wrong dtype or too small; combine output of the wrong shape")
+    q, kc, vc, lens = [dev(t) for t in decode_inputs(1, 300, base=8700)]
+    need = gqa.decode_workspace_bytes(1, 300, 32, 8, 128)
+    with pytest.raises(ValueError):
+        gqa.decode(q, kc, vc, lens, workspace=torch.zeros(need, dtype=torch.uint8))        # host memory
+    with pytest.raises(ValueError):
+        gqa.decode(q, kc, vc, lens, workspace=torch.zeros(need // 4 + 1, dtype=torch.int32, device="cuda:0"))
+    with pytest.raises(gqa.GqaAttnError):
+        gqa.decode(q, kc, vc, lens, workspace=torch.zeros(64, dtype=torch.uint8, device="cuda:0"))
+    o_part, lse, ws = gqa.decode_partials(q, kc, vc, lens, 128)
+    with pytest.raises(ValueError):
+        gqa.decode_combine(ws, 1, 32, 3, out=torch.empty((1, 32, 64), dtype=torch.bfloat16, device="cuda:0"))
+    with pytest.raises(ValueError):
+        gqa.decode_combine(ws.cpu(), 1, 32, 3)
+    good = gqa.decode_combine(ws, 1, 32, 3)
+    torch.cuda.synchronize()
+    assert torch.isfinite(good.float()).all()
