@@ -142,12 +142,14 @@ def decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, lens: to
 
 
 def prefill_plan(B: int, S: int, Hq: int, Hkv: int, D: int = D_SUPPORTED):
-    """(waves per workgroup, workgroups) the library launches for this prefill shape."""
+    """(waves per workgroup, workgroups, key splits) the library launches for this prefill shape."""
     waves = ctypes.c_int(0)
     wgs = ctypes.c_int(0)
-    rc = _lib.get().gqa_attn_prefill_plan(B, S, Hq, Hkv, D, ctypes.byref(waves), ctypes.byref(wgs))
+    ks = ctypes.c_int(0)
+    rc = _lib.get().gqa_attn_prefill_plan(B, S, Hq, Hkv, D, ctypes.byref(waves), ctypes.byref(wgs),
+                                          ctypes.byref(ks))
     _lib.check(rc, "gqa_attn_prefill_plan")
-    return waves.value, wgs.value
+    return waves.value, wgs.value, ks.value
 
 
 def decode_plan(B: int, L: int, Hq: int, Hkv: int, D: int = D_SUPPORTED):

@@ -29,7 +29,7 @@ SIGNATURES = {
     "gqa_attn_prefill": (_c_int, [_ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
                                   _c_float, _c_int, _ptr]),
     "gqa_attn_prefill_plan": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int,
-                                       ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
+                                       ctypes.POINTER(_c_int), ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
     "gqa_attn_decode": (_c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _c_float, _ptr]),
     "gqa_attn_decode_plan": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int,

@@ -216,6 +216,7 @@ int plan_prefill(int B, int S, int Hq, int Hkv, int D, float scale, gqa::Prefill
   a->nrb = (S + 31) / 32;
   const long long units = (long long)a->G * a->nrb;
   a->nw = gqa::prefill_waves(B, S, Hkv, a->G);
+  a->ks = gqa::prefill_key_splits(B, S, Hkv, a->G);
   const long long wgs = (units + a->nw - 1) / a->nw;
   const long long grid = wgs * (long long)B * Hkv;
   if (grid > 0x7fffffffLL) return GQA_ATTN_ERR_DIM;
@@ -242,12 +243,14 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, void* out,
   return GQA_ATTN_OK;
 }
 
-int gqa_attn_prefill_plan(int B, int S, int Hq, int Hkv, int D, int* waves, int* workgroups) {
+int gqa_attn_prefill_plan(int B, int S, int Hq, int Hkv, int D, int* waves, int* workgroups,
+                          int* key_splits) {
   gqa::PrefillArgs a;
   const int e = plan_prefill(B, S, Hq, Hkv, D, 1.0f, &a);
   if (e) return e;
-  if (waves) *waves = a.nw;
+  if (waves) *waves = a.nw * a.ks;
   if (workgroups) *workgroups = a.wgs_per_slot * a.nslots;
+  if (key_splits) *key_splits = a.ks;
   return GQA_ATTN_OK;
 }
 

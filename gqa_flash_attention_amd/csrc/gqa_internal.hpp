@@ -14,7 +14,8 @@ struct PrefillArgs {
   uint16_t* out;         // [B, S, Hq, D]
   int B, S, Hq, Hkv, G;  // G = Hq / Hkv
   int nrb;               // 32-row query blocks per sequence: ceil(S / 32)
-  int nw;                // waves per workgroup (4 or 8; prefill_waves)
+  int nw;                // (row block, head) units per workgroup (4 or 8; prefill_waves)
+  int ks;                // key splits per unit (1, or 2 in the 4-unit form; prefill_key_splits)
   int wgs_per_slot;      // workgroups per (b, kv head): ceil(G * nrb / nw)
   int nslots;            // B * Hkv
   float c;               // scale * log2(e)
@@ -44,8 +45,10 @@ struct CombineArgs {
 };
 
 // Each returns a hipError_t value (0 = success) from the launch.
-// Waves per prefill workgroup the library uses for this shape (4 or 8).
+// Units (one wave each per key split) per prefill workgroup for this shape (4 or 8), and
+// the key splits of the 4-unit form (1 or 2); a workgroup has nw * ks waves.
 int prefill_waves(int B, int S, int Hkv, int G);
+int prefill_key_splits(int B, int S, int Hkv, int G);
 int launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
 // fused = true: split, then merge in the last-arriving workgroup, writing `out`.
 // fused = false: only the per-chunk partials (o_part, lse).

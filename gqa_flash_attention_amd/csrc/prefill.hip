@@ -22,8 +22,11 @@
 // has freed. The 8-wave form copies each tile once for 256 query rows instead of 128
 // and meets a barrier every other tile; with a single workgroup per CU a barrier idles
 // the whole CU, so halving them is what makes it pay (3-4% at 16K-32K keys on MI355X).
-// It needs at least 4 workgroups per CU to balance the causal triangle, so short
-// prompts keep the 4-wave form. Scores are
+// It needs at least 4 workgroups per CU to balance the causal triangle, so shorter
+// prompts keep the 4-wave form. Where even that grid holds at most 2 workgroups per CU,
+// the critical path is the longest query tile's walk over its keys; there a key-split
+// form (prefill_split_kernel, below) gives each 4-wave unit set a second set of 4 waves
+// that walks the other half of the key tiles. Scores are
 // computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K from LDS is the A
 // operand, the wave's Q rows stay in registers as the B operand. In that layout each
 // lane's 32 scores of a 64-key tile belong to its own query row, so the row max needs
@@ -41,6 +44,143 @@
 namespace gqa {
 
 constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 units (p <= 2^8)
+
+// Online-softmax state of one wave's 32 query rows: running max m (log2 units), this
+// lane's partial sum l over its half of the keys, and O^T (lane: one query row, 64 of its
+// 128 output columns), all relative to m.
+struct RowState {
+  float m;
+  float l;
+  f32x16 o[4];
+};
+
+// One 64-key tile of K (kt) and V (vt) in LDS, key tile index t, for the wave whose 32
+// query rows start at q0 and whose Q fragments are qreg (B operand, 8 k-steps of 16 d).
+template <bool CAUSAL, bool POS>
+__device__ __forceinline__ void attend_tile(const GQA_LDS uint8_t* kt, const GQA_LDS uint8_t* vt,
+                                            int t, int q0, int S, float c, int lane,
+                                            const bf16x8 (&qreg)[8], RowState& st) {
+  const int h = lane >> 5;
+  const int qi = lane & 31;
+  // S^T[key][query] for the tile's 64 keys, two 32-key blocks. The K operand reads run
+  // 4 k-steps ahead of the MFMAs that consume them. The wave raises its issue priority
+  // while it feeds the matrix cores, so that on a SIMD shared with a wave doing softmax
+  // work the MFMA stream is not starved.
+  __builtin_amdgcn_s_setprio(1);
+  f32x16 s0 = f32x16{}, s1 = f32x16{};
+  bf16x8 ka[4], kb[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    ka[ks] = lds_read_k(kt, qi, 2 * ks + h);
+    kb[ks] = lds_read_k(kt, 32 + qi, 2 * ks + h);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    s0 = mfma32(ka[ks & 3], qreg[ks], s0);
+    s1 = mfma32(kb[ks & 3], qreg[ks], s1);
+    if (ks + 4 < 8) {
+      ka[ks & 3] = lds_read_k(kt, qi, 2 * (ks + 4) + h);
+      kb[ks & 3] = lds_read_k(kt, 32 + qi, 2 * (ks + 4) + h);
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+  if (!POS) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { s0[v] *= c; s1[v] *= c; }
+  }
+  // Mask keys this lane's query may not see: above the diagonal (causal) or past S.
+  const int key0 = t * kTileRows;
+  const bool need_mask = CAUSAL ? (key0 + kTileRows - 1 > q0) : (key0 + kTileRows > S);
+  if (need_mask) {
+    const int lim = CAUSAL ? (q0 + qi) : (S - 1);   // largest visible key
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int kk = key0 + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (kk > lim) s0[v] = -INFINITY;
+      if (kk + 32 > lim) s1[v] = -INFINITY;
+    }
+  }
+  float mx = s0[0];
+#pragma unroll
+  for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s0[v]);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s1[v]);
+  mx = halves_max(mx);
+  const float m_cand = fmaxf(st.m, POS ? mx * c : mx);
+  const bool upd = m_cand > st.m + kTau;
+  if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+    const float m_new = upd ? m_cand : st.m;
+    const float alpha = (m_new == st.m) ? 1.f : exp2_fast(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) st.o[mb] *= alpha;
+    st.m = m_new;
+  }
+  const float neg_m = -st.m;
+  // O^T[d][query] += V^T[d][key] P^T[key][query], 4 k-steps of 16 keys. P^T is the B
+  // operand straight from the accumulator layout (k index 8h+u <-> key
+  // 16t4 + 8(u/4) + 4h + u%4). For d-block mb the A operand has lane l holding
+  // d = 32mb + l%32 and keys 16t4 + 4(l/32) + {0..3, 8..11}, read transposed from LDS.
+  // Each step's probabilities are formed just before its MFMAs and the next step's V
+  // reads are already in flight, so exp work overlaps the matrix cores.
+  const int g16 = lane >> 4;
+  const int li = lane & 15;
+  const int vrow = 4 * (g16 >> 1) + (li >> 2);
+  const int vcol = 16 * (g16 & 1) + 4 * (li & 3);
+  s16x4 vlo[4], vhi[4];
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    vlo[mb] = lds_read_v_tr(vt, vrow, 32 * mb + vcol);
+    vhi[mb] = lds_read_v_tr(vt, 8 + vrow, 32 * mb + vcol);
+  }
+#pragma unroll
+  for (int t4 = 0; t4 < 4; ++t4) {
+    const f32x16& sb = (t4 < 2) ? s0 : s1;
+    const int o = 8 * (t4 & 1);
+    float e[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      e[u] = exp2_fast(POS ? __builtin_fmaf(sb[o + u], c, neg_m) : sb[o + u] + neg_m);
+    const bf16x8 p = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+    st.l = sum_bf16x8(p, st.l);
+    s16x4 nlo[4], nhi[4];
+    if (t4 < 3) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        nlo[mb] = lds_read_v_tr(vt, 16 * (t4 + 1) + vrow, 32 * mb + vcol);
+        nhi[mb] = lds_read_v_tr(vt, 16 * (t4 + 1) + 8 + vrow, 32 * mb + vcol);
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) st.o[mb] = mfma32(join_bf16x8(vlo[mb], vhi[mb]), p, st.o[mb]);
+    if (t4 < 3) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) { vlo[mb] = nlo[mb]; vhi[mb] = nhi[mb]; }
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// Row qpos of head `head`: this lane's 64 output columns of O / l as bf16.
+__device__ __forceinline__ void store_rows(const PrefillArgs& a, int b, int qpos, int head, int h,
+                                           float l_tot, const RowState& st) {
+  const float inv = 1.0f / l_tot;
+  uint16_t* op = a.out + (((size_t)b * a.S + qpos) * a.Hq + head) * kD + 4 * h;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq) {
+      typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+      u16x4 w;
+      w[0] = bf16_bits(st.o[mb][4 * vq + 0] * inv);
+      w[1] = bf16_bits(st.o[mb][4 * vq + 1] * inv);
+      w[2] = bf16_bits(st.o[mb][4 * vq + 2] * inv);
+      w[3] = bf16_bits(st.o[mb][4 * vq + 3] * inv);
+      *(u16x4*)(op + 32 * mb + 8 * vq) = w;
+    }
+  }
+}
 
 template <bool CAUSAL, bool POS, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -114,12 +254,11 @@ void prefill_kernel(PrefillArgs a) {
   for (int t = 1; t < P; ++t)
     if (t < nt) issue_tile(t, kbuf(t), vbuf(t));
 
-  const float c = a.c;
-  float m_run = -INFINITY;
-  float l_part = 0.f;
-  f32x16 oacc[4];
+  RowState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) oacc[mb] = f32x16{};
+  for (int mb = 0; mb < 4; ++mb) st.o[mb] = f32x16{};
 
   // One key tile. BUF = t % NST selects the ring stage at compile time.
   auto step = [&](int t, auto bufc) {
@@ -141,104 +280,7 @@ void prefill_kernel(PrefillArgs a) {
     }
     if (!active || t >= own_nt) return;
 
-    // S^T[key][query] for the tile's 64 keys, two 32-key blocks. The K operand reads run
-    // 4 k-steps ahead of the MFMAs that consume them. The wave raises its issue priority
-    // while it feeds the matrix cores, so that on a SIMD shared with a wave doing softmax
-    // work the MFMA stream is not starved.
-    __builtin_amdgcn_s_setprio(1);
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
-    bf16x8 ka[4], kb[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      ka[ks] = lds_read_k(kt, qi, 2 * ks + h);
-      kb[ks] = lds_read_k(kt, 32 + qi, 2 * ks + h);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      s0 = mfma32(ka[ks & 3], qreg[ks], s0);
-      s1 = mfma32(kb[ks & 3], qreg[ks], s1);
-      if (ks + 4 < 8) {
-        ka[ks & 3] = lds_read_k(kt, qi, 2 * (ks + 4) + h);
-        kb[ks & 3] = lds_read_k(kt, 32 + qi, 2 * (ks + 4) + h);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-    if (!POS) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) { s0[v] *= c; s1[v] *= c; }
-    }
-    // Mask keys this lane's query may not see: above the diagonal (causal) or past S.
-    const int key0 = t * kTileRows;
-    const bool need_mask = CAUSAL ? (key0 + kTileRows - 1 > q0) : (key0 + kTileRows > a.S);
-    if (need_mask) {
-      const int lim = CAUSAL ? (q0 + qi) : (a.S - 1);   // largest visible key
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kk = key0 + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (kk > lim) s0[v] = -INFINITY;
-        if (kk + 32 > lim) s1[v] = -INFINITY;
-      }
-    }
-    float mx = s0[0];
-#pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s0[v]);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s1[v]);
-    mx = halves_max(mx);
-    const float m_cand = fmaxf(m_run, POS ? mx * c : mx);
-    const bool upd = m_cand > m_run + kTau;
-    if (__builtin_amdgcn_ballot_w64(upd) != 0) {
-      const float m_new = upd ? m_cand : m_run;
-      const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m_run - m_new);
-      l_part *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) oacc[mb] *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = -m_run;
-    // O^T[d][query] += V^T[d][key] P^T[key][query], 4 k-steps of 16 keys. P^T is the B
-    // operand straight from the accumulator layout (k index 8h+u <-> key
-    // 16t4 + 8(u/4) + 4h + u%4). For d-block mb the A operand has lane l holding
-    // d = 32mb + l%32 and keys 16t4 + 4(l/32) + {0..3, 8..11}, read transposed from LDS.
-    // Each step's probabilities are formed just before its MFMAs and the next step's V
-    // reads are already in flight, so exp work overlaps the matrix cores.
-    const int g16 = lane >> 4;
-    const int li = lane & 15;
-    const int vrow = 4 * (g16 >> 1) + (li >> 2);
-    const int vcol = 16 * (g16 & 1) + 4 * (li & 3);
-    s16x4 vlo[4], vhi[4];
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      vlo[mb] = lds_read_v_tr(vt, vrow, 32 * mb + vcol);
-      vhi[mb] = lds_read_v_tr(vt, 8 + vrow, 32 * mb + vcol);
-    }
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const f32x16& sb = (t4 < 2) ? s0 : s1;
-      const int o = 8 * (t4 & 1);
-      float e[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        e[u] = exp2_fast(POS ? __builtin_fmaf(sb[o + u], c, neg_m) : sb[o + u] + neg_m);
-      const bf16x8 p = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-      l_part = sum_bf16x8(p, l_part);
-      s16x4 nlo[4], nhi[4];
-      if (t4 < 3) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          nlo[mb] = lds_read_v_tr(vt, 16 * (t4 + 1) + vrow, 32 * mb + vcol);
-          nhi[mb] = lds_read_v_tr(vt, 16 * (t4 + 1) + 8 + vrow, 32 * mb + vcol);
-        }
-      }
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) oacc[mb] = mfma32(join_bf16x8(vlo[mb], vhi[mb]), p, oacc[mb]);
-      if (t4 < 3) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) { vlo[mb] = nlo[mb]; vhi[mb] = nhi[mb]; }
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
+    attend_tile<CAUSAL, POS>(kt, vt, t, q0, a.S, a.c, lane, qreg, st);
   };
 
   for (int t = 0; t < nt; t += NST) {
@@ -249,25 +291,138 @@ void prefill_kernel(PrefillArgs a) {
   }
 
   // Epilogue: the two halves of the wave hold disjoint keys of the same rows.
-  const float l_tot = halves_sum(l_part);
+  const float l_tot = halves_sum(st.l);
   if (!active) return;
   const int qpos = q0 + qi;
   if (qpos >= a.S) return;
-  const float inv = 1.0f / l_tot;
-  uint16_t* op = a.out + (((size_t)b * a.S + qpos) * a.Hq + head) * kD + 4 * h;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-    for (int vq = 0; vq < 4; ++vq) {
-      typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
-      u16x4 w;
-      w[0] = bf16_bits(oacc[mb][4 * vq + 0] * inv);
-      w[1] = bf16_bits(oacc[mb][4 * vq + 1] * inv);
-      w[2] = bf16_bits(oacc[mb][4 * vq + 2] * inv);
-      w[3] = bf16_bits(oacc[mb][4 * vq + 3] * inv);
-      *(u16x4*)(op + 32 * mb + 8 * vq) = w;
+  store_rows(a, b, qpos, head, h, l_tot, st);
+}
+
+// Key-split form, for grids too small to fill the GPU (short prompts). A workgroup of 8
+// waves serves the same 4 (row block, head) units as the 4-wave form, but its two halves
+// of 4 waves take different halves of the units' key tiles, the first ceil(nt/2) and the
+// rest, one tile per step through a 2-stage ring of their own. Each half keeps its own
+// online softmax; at the end half 1 hands (m, l, O) to half 0 through LDS, and half 0
+// merges the two by their log-sum-exp weights and writes the rows. The longest job of the
+// causal triangle then takes half the steps, and every SIMD holds two waves.
+template <bool CAUSAL, bool POS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_split_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv[2][2][2][kTileBytes];   // [half][stage][K/V]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = wave >> 2;   // which half of the key tiles this wave streams
+  const int sub = wave & 3;     // the wave's unit within the workgroup
+  const int h = lane >> 5;
+  const int qi = lane & 31;
+
+  // Workgroup -> (batch, KV head, query tile) exactly as in the 4-wave form.
+  const int bid = blockIdx.x;
+  const int slot = bid % a.nslots;
+  const int j = bid / a.nslots;
+  const int wg = CAUSAL ? (a.wgs_per_slot - 1 - j) : j;
+  const int b = slot / a.Hkv;
+  const int g = slot % a.Hkv;
+  const int nunits = a.G * a.nrb;
+  const int unit = 4 * wg + sub;
+  const bool active = unit < nunits;
+  const int rb = active ? unit / a.G : 0;
+  const int head = g * a.G + (active ? unit % a.G : 0);
+  const int q0 = rb * 32;
+
+  const int last_unit = min(4 * wg + 3, nunits - 1);
+  const int kv_end = CAUSAL ? min(a.S, (last_unit / a.G) * 32 + 32) : a.S;
+  const int nt = (kv_end + kTileRows - 1) / kTileRows;
+  const int mid = (nt + 1) / 2;               // half 0: tiles [0, mid); half 1: [mid, nt)
+  const int t_begin = half ? mid : 0;
+  const int t_end = half ? nt : mid;
+  const int own_end = CAUSAL ? min(a.S, q0 + 32) : a.S;
+  const int own_nt = (own_end + kTileRows - 1) / kTileRows;
+
+  const size_t kv_stride = (size_t)a.Hkv * kD;
+  const uint16_t* kbase = a.k + ((size_t)b * a.S * a.Hkv + g) * kD;
+  const uint16_t* vbase = a.v + ((size_t)b * a.S * a.Hkv + g) * kD;
+
+  TileCopy<4> copy;
+  copy.init(kv_stride, sub, lane);
+  auto kbuf = [&](int stage) { return (GQA_LDS uint8_t*)lds_kv[half][stage][0]; };
+  auto vbuf = [&](int stage) { return (GQA_LDS uint8_t*)lds_kv[half][stage][1]; };
+  // Copies of tile t by this half's 4 waves.
+  auto issue_tile = [&](int t, GQA_LDS uint8_t* kd, GQA_LDS uint8_t* vd) {
+    const int r0 = t * kTileRows;
+    if (kv_end - r0 >= kTileRows) {
+      copy.issue_full(kd, vd, kbase + (size_t)r0 * kv_stride, vbase + (size_t)r0 * kv_stride, sub);
+    } else {
+      stage_tile<4, false>(kd, kbase + (size_t)r0 * kv_stride, kv_stride, kv_end - r0, sub, lane);
+      stage_tile<4, true>(vd, vbase + (size_t)r0 * kv_stride, kv_stride, kv_end - r0, sub, lane);
     }
+  };
+
+  if (t_begin < t_end) issue_tile(t_begin, kbuf(0), vbuf(0));
+  bf16x8 qreg[8];
+  {
+    const int qrow = min(q0 + qi, a.S - 1);
+    const uint16_t* qp = a.q + (((size_t)b * a.S + qrow) * a.Hq + head) * kD + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qreg[ks] = *(const bf16x8*)(qp + 16 * ks);
   }
+  wait_vmcnt<0>();
+
+  RowState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) st.o[mb] = f32x16{};
+
+  // Step i: this half's tile t = t_begin + i. Both halves take the same barrier each step
+  // (half 1 has at most as many tiles as half 0); their rings are disjoint. The barrier
+  // publishes tile t and frees the stage tile t - 1 used, which takes tile t + 1.
+  auto step = [&](int i, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int t = t_begin + i;
+    wait_vmcnt<0>();
+    tile_barrier();
+    if (t + 1 < t_end) issue_tile(t + 1, kbuf(BUF ^ 1), vbuf(BUF ^ 1));
+    if (!active || t >= t_end || t >= own_nt) return;
+    attend_tile<CAUSAL, POS>(kbuf(BUF), vbuf(BUF), t, q0, a.S, a.c, lane, qreg, st);
+  };
+  for (int i = 0; i < mid; i += 2) {
+    step(i, std::integral_constant<int, 0>{});
+    if (i + 1 < mid) step(i + 1, std::integral_constant<int, 1>{});
+  }
+
+  // Merge. Every copy has landed (each was waited for before the barrier of its step) and
+  // no wave reads the rings any more, so they hold half 1's state: per lane its 64 O
+  // values, m and l, at a stride of 66 floats.
+  __syncthreads();
+  float* const xs = (float*)lds_kv + ((size_t)sub * 64 + lane) * 66;
+  if (half == 1) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) xs[16 * mb + v] = st.o[mb][v];
+    xs[64] = st.m;
+    xs[65] = st.l;
+  }
+  __syncthreads();
+  if (half == 1 || !active) return;
+  {
+    // Both parts are relative to their own m; an empty part (m = -inf) weighs nothing.
+    const float m1 = xs[64];
+    const float mm = fmaxf(st.m, m1);
+    const float w0 = (st.m == -INFINITY) ? 0.f : exp2_fast(st.m - mm);
+    const float w1 = (m1 == -INFINITY) ? 0.f : exp2_fast(m1 - mm);
+    st.l = w0 * st.l + w1 * xs[65];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st.o[mb][v] = w0 * st.o[mb][v] + w1 * xs[16 * mb + v];
+  }
+  const float l_tot = halves_sum(st.l);
+  const int qpos = q0 + qi;
+  if (qpos >= a.S) return;
+  store_rows(a, b, qpos, head, h, l_tot, st);
 }
 
 int prefill_waves(int B, int S, int Hkv, int G) {
@@ -276,6 +431,16 @@ int prefill_waves(int B, int S, int Hkv, int G) {
   const long long units = (long long)G * ((S + 31) / 32);
   const long long wgs8 = (long long)B * Hkv * ((units + 7) / 8);
   return wgs8 >= 4 * 256 ? 8 : 4;
+}
+
+int prefill_key_splits(int B, int S, int Hkv, int G) {
+  // Split the key tiles over two half-workgroups when the 4-wave grid holds at most 2
+  // workgroups per CU and the longest job has at least 8 key tiles (B = 1, 32 query and
+  // 8 KV heads: 512 <= S <= 2048). On MI355X that is 5-21% faster there; at 3000-4096
+  // keys, with 3-4 workgroups per CU, the 4-wave form is 7-8% faster.
+  const long long units = (long long)G * ((S + 31) / 32);
+  const long long wgs4 = (long long)B * Hkv * ((units + 3) / 4);
+  return (prefill_waves(B, S, Hkv, G) == 4 && wgs4 <= 2 * 256 && S >= 512) ? 2 : 1;
 }
 
 template <int NW>
@@ -292,9 +457,23 @@ static void launch_prefill_nw(const PrefillArgs& a, bool causal, hipStream_t str
   }
 }
 
+static void launch_prefill_split(const PrefillArgs& a, bool causal, hipStream_t stream) {
+  const dim3 grid((unsigned)((size_t)a.nslots * a.wgs_per_slot));
+  const dim3 block(512);
+  const bool pos = a.c > 0.f;
+  if (causal) {
+    if (pos) hipLaunchKernelGGL((prefill_split_kernel<true, true>), grid, block, 0, stream, a);
+    else     hipLaunchKernelGGL((prefill_split_kernel<true, false>), grid, block, 0, stream, a);
+  } else {
+    if (pos) hipLaunchKernelGGL((prefill_split_kernel<false, true>), grid, block, 0, stream, a);
+    else     hipLaunchKernelGGL((prefill_split_kernel<false, false>), grid, block, 0, stream, a);
+  }
+}
+
 int launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream) {
-  if (a.nw == 8) launch_prefill_nw<8>(a, causal, stream);
-  else           launch_prefill_nw<4>(a, causal, stream);
+  if (a.nw == 8)      launch_prefill_nw<8>(a, causal, stream);
+  else if (a.ks == 2) launch_prefill_split(a, causal, stream);
+  else                launch_prefill_nw<4>(a, causal, stream);
   return (int)hipGetLastError();
 }
 

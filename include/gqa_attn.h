@@ -67,14 +67,21 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, void* out,
                      void* stream);
 
 /*
- * The launch gqa_attn_prefill uses for this shape. Each wave owns 32 query rows
- * of one head; *waves (4 or 8) is the number of waves per workgroup, all serving
- * one KV head, and *workgroups the size of the grid. The 8-wave form is taken
- * once its grid holds at least 4 workgroups per CU (for B = 1 with 32 query and
- * 8 KV heads: S > 8128). Either
- * output may be NULL. Returns the same shape errors as gqa_attn_prefill.
+ * The launch gqa_attn_prefill uses for this shape. A unit is 32 query rows of
+ * one head; a workgroup serves 4 or 8 units of one KV head. *key_splits is 1
+ * (one wave per unit, which streams all of the unit's key tiles) or 2 (two
+ * waves per unit, each streaming half of them; their softmax states are merged
+ * by log-sum-exp weights before the rows are written). *waves is the workgroup
+ * size in waves (units x key splits) and *workgroups the size of the grid.
+ * The 8-unit form is taken once its grid holds at least 4 workgroups per CU;
+ * the key split when the 4-unit grid holds at most 2 per CU and S >= 512.
+ * For B = 1 with 32 query and 8 KV heads: S < 512 gives (4, 1),
+ * 512 <= S <= 2048 gives (8, 2), S <= 8128 gives (4, 1), larger S (8, 1) as
+ * (waves, key_splits). Any output may be NULL. Returns the same shape errors
+ * as gqa_attn_prefill.
  */
-int gqa_attn_prefill_plan(int B, int S, int Hq, int Hkv, int D, int* waves, int* workgroups);
+int gqa_attn_prefill_plan(int B, int S, int Hq, int Hkv, int D, int* waves, int* workgroups,
+                          int* key_splits);
 
 /*
  * One-token decode against a KV cache, split along the cache.

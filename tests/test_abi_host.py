@@ -148,19 +148,29 @@ def test_decode_plan_and_workspace_size(lib):
 def test_prefill_plan(lib):
     waves = ctypes.c_int(0)
     wgs = ctypes.c_int(0)
-    # batch 1, Llama-3-8B heads: 4-wave workgroups (2 per CU) below 8K keys, 8 from there
-    for S, want in ((1, 4), (512, 4), (4096, 4), (8128, 4), (8129, 8), (8192, 8), (32768, 8)):
-        assert lib.gqa_attn_prefill_plan(1, S, 32, 8, 128, ctypes.byref(waves), ctypes.byref(wgs)) == 0
-        assert waves.value == want, S
+    ks = ctypes.c_int(0)
+    # batch 1, Llama-3-8B heads: (waves, key splits, units per workgroup). 4 units of one
+    # wave each below 512 keys; the key split (4 units x 2 waves) up to 2048 keys, while
+    # the 4-unit grid holds at most 2 workgroups per CU; 4 units again up to 8128; then 8.
+    for S, want in ((1, (4, 1, 4)), (511, (4, 1, 4)), (512, (8, 2, 4)), (1000, (8, 2, 4)),
+                    (2048, (8, 2, 4)), (2049, (4, 1, 4)), (4096, (4, 1, 4)), (8128, (4, 1, 4)),
+                    (8129, (8, 1, 8)), (8192, (8, 1, 8)), (32768, (8, 1, 8))):
+        assert lib.gqa_attn_prefill_plan(1, S, 32, 8, 128, ctypes.byref(waves), ctypes.byref(wgs),
+                                         ctypes.byref(ks)) == 0
+        assert (waves.value, ks.value) == want[:2], S
         units = 4 * -(-S // 32)
-        assert wgs.value == 8 * -(-units // want)
-    # a batch reaches 4 workgroups per CU sooner
-    assert lib.gqa_attn_prefill_plan(8, 1000, 32, 8, 128, ctypes.byref(waves), None) == 0
-    assert waves.value == 8
-    assert lib.gqa_attn_prefill_plan(1, 100, 32, 8, 128, None, None) == 0
-    assert lib.gqa_attn_prefill_plan(0, 100, 32, 8, 128, None, None) == _lib.ERR_DIM
-    assert lib.gqa_attn_prefill_plan(1, 100, 32, 8, 64, None, None) == _lib.ERR_UNSUPPORTED
-    assert lib.gqa_attn_prefill_plan(1, 100, 30, 8, 128, None, None) == _lib.ERR_DIM
+        assert wgs.value == 8 * -(-units // want[2]), S
+    # a batch reaches 4 workgroups per CU sooner, and 2 per CU sooner
+    assert lib.gqa_attn_prefill_plan(8, 1000, 32, 8, 128, ctypes.byref(waves), None, ctypes.byref(ks)) == 0
+    assert (waves.value, ks.value) == (8, 1)
+    assert lib.gqa_attn_prefill_plan(4, 1000, 32, 8, 128, ctypes.byref(waves), None, ctypes.byref(ks)) == 0
+    assert (waves.value, ks.value) == (4, 1)
+    assert lib.gqa_attn_prefill_plan(2, 1000, 32, 8, 128, ctypes.byref(waves), None, ctypes.byref(ks)) == 0
+    assert (waves.value, ks.value) == (8, 2)
+    assert lib.gqa_attn_prefill_plan(1, 100, 32, 8, 128, None, None, None) == 0
+    assert lib.gqa_attn_prefill_plan(0, 100, 32, 8, 128, None, None, None) == _lib.ERR_DIM
+    assert lib.gqa_attn_prefill_plan(1, 100, 32, 8, 64, None, None, None) == _lib.ERR_UNSUPPORTED
+    assert lib.gqa_attn_prefill_plan(1, 100, 30, 8, 128, None, None, None) == _lib.ERR_DIM
 
 
 def test_release_without_any_workspace_is_harmless(lib):
