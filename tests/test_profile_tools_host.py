@@ -1,0 +1,103 @@
+"""The two counter post-processors on synthetic rocprofv3 output (CPU only): the per-launch
+HBM bytes of traffic.py and the clock / MFMA utilisation / FLOP ratio / hit rate of
+counters.py are recomputed here from values chosen so every figure is known in advance."""
+
+import csv
+import os
+
+import pytest
+
+from gqa_flash_attention_amd import counters, traffic
+
+import bench
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value",
+          "Start_Timestamp", "End_Timestamp"]
+PREFILL = "void gqa::prefill_kernel<true, true, 8>(gqa::PrefillArgs)"
+DECODE = "void gqa::decode_kernel<4, true, true>(gqa::DecodeArgs)"
+
+
+def _write(d, rows, agent=True):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "pmc_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+    if agent:
+        with open(os.path.join(d, "pmc_agent_info.csv"), "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Agent_Type", "Num_Xcc", "Simd_Count"])
+            w.writeheader()
+            w.writerow({"Agent_Type": "CPU", "Num_Xcc": 0, "Simd_Count": 0})
+            w.writerow({"Agent_Type": "GPU", "Num_Xcc": 8, "Simd_Count": 1024})
+
+
+def _row(did, name, counter, value, t0, ns, grid=1024):
+    return {"Dispatch_Id": did, "Kernel_Name": name, "Grid_Size": grid, "Counter_Name": counter,
+            "Counter_Value": value, "Start_Timestamp": t0, "End_Timestamp": t0 + ns}
+
+
+def test_traffic_scales_by_the_calibration_copy(tmp_path):
+    S, L = 2048, 4096
+    mib = 16
+    fetch, write = [], []
+    # the calibration copy: FETCH_SIZE reads 2x the copied KiB, WRITE_SIZE 1x
+    fetch.append(_row(1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 2 * mib * 1024, 0, 10, grid=4096))
+    write.append(_row(1, "__amd_rocclr_copyBuffer", "WRITE_SIZE", mib * 1024, 0, 10, grid=4096))
+    for i, (pf, df) in enumerate(((3000.0, 500.0), (3100.0, 520.0))):
+        fetch += [_row(10 + 2 * i, PREFILL, "FETCH_SIZE", pf, 100, 10), _row(11 + 2 * i, DECODE, "FETCH_SIZE", df, 200, 10)]
+        write += [_row(10 + 2 * i, PREFILL, "WRITE_SIZE", 700.0, 100, 10), _row(11 + 2 * i, DECODE, "WRITE_SIZE", 4.0, 200, 10)]
+    _write(tmp_path / "f", fetch, agent=False)
+    _write(tmp_path / "w", write, agent=False)
+    res = traffic.summarize(str(tmp_path / "f"), str(tmp_path / "w"), mib, S, L)
+    assert res["calibration"]["fetch_scale"] == pytest.approx(0.5)
+    assert res["calibration"]["write_scale"] == pytest.approx(1.0)
+    p = res["kernels"][f"prefill_S{S}"]
+    assert p["fetch_bytes"] == pytest.approx(3050.0 * 1024 * 0.5)
+    assert p["write_bytes"] == pytest.approx(700.0 * 1024)
+    assert p["algorithmic_bytes"] == bench.prefill_bytes(S)
+    d = res["kernels"][f"decode_L{L}"]
+    assert d["hbm_bytes_per_launch"] == pytest.approx(510.0 * 1024 * 0.5 + 4.0 * 1024)
+    assert d["ratio_to_algorithmic"] == pytest.approx(d["hbm_bytes_per_launch"] / bench.decode_bytes(L))
+
+
+def test_counters_clock_utilisation_and_flop_ratio(tmp_path):
+    S, L = 4096, 8192
+    ns_p, ns_d = 2_000_000, 40_000          # dispatch durations
+    ghz = 1.9                               # shader clock the GRBM counts imply
+    util = 0.6                              # MFMA busy fraction of SIMD cycles
+    sq, tcc = [], []
+    did = 0
+    for rep in range(5):                    # 2 warm-up dispatches per kernel, then 3
+        for name, ns, flop_ratio in ((PREFILL, ns_p, 1.002), (DECODE, ns_d, 0.0)):
+            did += 1
+            t0 = 1_000_000_000 * did
+            cyc = ghz * ns                  # one XCD's busy cycles
+            for x in range(8):              # GRBM_GUI_ACTIVE: one row per XCD
+                sq.append(_row(did, name, "GRBM_GUI_ACTIVE", cyc, t0, ns))
+                tcc.append(_row(did, name, "GRBM_GUI_ACTIVE", cyc, t0, ns))
+            mops = flop_ratio * bench.prefill_flops(S) / 512 if name == PREFILL else 0.0
+            for se in range(4):             # SQ counters: rows per shader engine, summed
+                sq.append(_row(did, name, "SQ_VALU_MFMA_BUSY_CYCLES", util * cyc * 1024 / 4, t0, ns))
+                sq.append(_row(did, name, "SQ_VALU_MFMA_COEXEC_CYCLES", 0.1 * cyc * 1024 / 4, t0, ns))
+                sq.append(_row(did, name, "SQ_INSTS_VALU_MFMA_MOPS_BF16", mops / 4, t0, ns))
+                sq.append(_row(did, name, "SQ_ACTIVE_INST_LDS", 1000.0, t0, ns))
+                sq.append(_row(did, name, "SQ_LDS_BANK_CONFLICT", 250.0 if name == DECODE else 0.0, t0, ns))
+            tcc.append(_row(did, name, "TCC_HIT_sum", 900.0 if name == PREFILL else 10.0, t0, ns))
+            tcc.append(_row(did, name, "TCC_MISS_sum", 100.0 if name == PREFILL else 990.0, t0, ns))
+    _write(tmp_path / "sq", sq)
+    _write(tmp_path / "tcc", tcc)
+    res = counters.summarize(str(tmp_path / "sq"), str(tmp_path / "tcc"), S, L, warmup=2)
+    assert (res["xcds"], res["simds"]) == (8, 1024)
+    p = res["kernels"][f"prefill_S{S}"]
+    d = res["kernels"][f"decode_L{L}"]
+    assert p["dispatches"] == d["dispatches"] == 3
+    assert p["clock_ghz"] == pytest.approx(ghz)
+    assert p["mfma_util"] == pytest.approx(util)
+    assert p["mfma_valu_coexec"] == pytest.approx(0.1)
+    assert p["mfma_flops_over_algorithmic"] == pytest.approx(1.002)
+    assert p["lds_bank_conflict_per_lds_cycle"] == 0.0
+    assert p["l2_hit_rate"] == pytest.approx(0.9)
+    assert d["lds_bank_conflict_per_lds_cycle"] == pytest.approx(0.25)
+    assert d["l2_hit_rate"] == pytest.approx(0.01)
+    assert d["duration_us"] == pytest.approx(40.0)
