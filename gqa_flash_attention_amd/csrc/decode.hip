@@ -463,4 +463,17 @@ int launch_decode_combine(const CombineArgs& a, hipStream_t stream) {
   return (int)hipGetLastError();
 }
 
+// Clears the merge counters of a new workspace. A kernel rather than hipMemsetAsync so
+// that a caller may capture the first decode on a stream into a HIP graph.
+__global__ __launch_bounds__(256) void zero_words_kernel(int* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0;
+}
+
+int launch_zero_words(int* p, size_t n, hipStream_t stream) {
+  if (n == 0) return 0;
+  const size_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream, p, n);
+  return (int)hipGetLastError();
+}
+
 }  // namespace gqa

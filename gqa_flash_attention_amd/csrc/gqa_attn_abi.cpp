@@ -125,8 +125,8 @@ int get_workspace(size_t need, size_t counters, hipStream_t stream, void** out) 
   }
   if (w.zero_counters < counters) {
     // The merge counters must start at zero; every completed decode leaves them zero.
-    e = hipMemsetAsync(w.ptr, 0, counters * sizeof(int), stream);
-    if (e != hipSuccess) return hip_fail("hipMemsetAsync(decode counters)", e);
+    const int ze = gqa::launch_zero_words((int*)w.ptr, counters, stream);
+    if (ze != 0) return hip_fail("zero_words launch (decode counters)", ze);
     w.zero_counters = counters;
   }
   *out = w.ptr;

@@ -54,6 +54,8 @@ int launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
 // fused = false: only the per-chunk partials (o_part, lse).
 int launch_decode(const DecodeArgs& a, bool fused, hipStream_t stream);
 int launch_decode_combine(const CombineArgs& a, hipStream_t stream);
+// Zeroes n int32 words at p (device memory) on `stream`.
+int launch_zero_words(int* p, size_t n, hipStream_t stream);
 
 // Measurement probes (probes.hip).
 int launch_probe_hbm_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);

@@ -102,9 +102,14 @@ int gqa_attn_prefill_plan(int B, int S, int Hq, int Hkv, int D, int* waves, int*
  * one fewer launch): the last workgroup to finish a (sequence, KV head) merges
  * it.
  * The split partials live in a library-owned workspace, cached per (device,
- * stream) and grown on demand: one hipMalloc (and a clear of the new buffer)
- * the first time a larger size is needed, none afterwards. Concurrent streams
- * never share a workspace.
+ * stream) and grown on demand: one hipMalloc (and a clear of the new buffer's
+ * counters by a small kernel) the first time a larger size is needed, none
+ * afterwards. Concurrent streams never share a workspace. To capture this call
+ * into a HIP graph, make one call of at least that size on the capturing
+ * stream first (a capture cannot allocate), or use gqa_attn_decode_ws; the
+ * graph then uses that stream's workspace wherever it is replayed, so a replay
+ * must not overlap other decodes on that stream. A stream's workspace is kept
+ * until gqa_attn_release, keyed by the stream handle.
  */
 int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
                     const int32_t* lens, void* out,

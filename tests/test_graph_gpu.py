@@ -1,8 +1,10 @@
 """The hot path under HIP graph capture. The prefill and a decode with a caller-owned
 workspace allocate nothing and enqueue only their kernels (the decode's merge counters are
-reset by the kernel itself, no memset), so both can be captured once and replayed. The
-graph is replayed several times with eager work between the replays (new inputs copied
-in place); every replay must equal, bit for bit, the same calls made eagerly."""
+reset by the kernel itself, no memset), so both can be captured once and replayed; so can
+a decode on the library's own workspace once an eager call on the capturing stream has
+created it. Each graph is replayed several times with eager work between the replays (new
+inputs copied in place); every replay must equal, bit for bit, the same calls made
+eagerly."""
 
 import pytest
 import torch
@@ -52,3 +54,30 @@ def test_prefill_and_decode_replay_from_a_graph():
         torch.cuda.synchronize()
         assert torch.equal(pout, want_p), f"replay {r}: prefill differs"
         assert torch.equal(dout, want_d), f"replay {r}: decode differs"
+
+
+def test_decode_on_the_library_workspace_replays_from_a_graph():
+    d = torch.device("cuda:0")
+    B, L = 1, 16384
+    _say(f"graph: decode B={B} L={L} on the library workspace of the capturing stream, 5 replays")
+    dq, kc, vc, lens = [t.to(d) for t in decode_inputs(B, L, base=9870)]
+    dout = torch.empty_like(dq)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gqa.decode(dq, kc, vc, lens, out=dout)   # creates and clears this stream's workspace
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        gqa.decode(dq, kc, vc, lens, out=dout)
+    torch.cuda.synchronize()
+    for r in range(5):
+        ndq, nkc, nvc, _ = [t.to(d) for t in decode_inputs(B, L, base=9880 + 10 * r)]
+        for dst, src in ((dq, ndq), (kc, nkc), (vc, nvc)):
+            dst.copy_(src)
+        want = gqa.decode(dq, kc, vc, lens)      # default stream, its own workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dout, want), f"replay {r}: decode differs"

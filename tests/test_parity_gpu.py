@@ -264,6 +264,22 @@ def test_decode_workspace_reused_across_calls():
     assert torch.equal(out1.cpu(), out3.cpu())
 
 
+def test_decode_large_batch_uses_more_than_the_minimum_counters():
+    # B * Hq = 4352 merge counters, past the 4096 every workspace holds at least; the
+    # library's workspace of this stream grows and its new counters are cleared
+    B, L = 136, 320
+    _say(f"decode B={B} L={L} on the library workspace: {B * HQ} merge counters")
+    lens = random_lens(B, 1, L, seed=8390)
+    q, kc, vc, lens = decode_inputs(B, L, base=8391, lens=lens, poison=True)
+    first = _decode_gpu(q, kc, vc, lens)
+    again = _decode_gpu(q, kc, vc, lens)
+    assert torch.equal(first, again)
+    rows = [0, 1, 67, B - 2, B - 1]
+    got = gpu_f64(first[rows])
+    want = oracle.decode(bf16_bits(q[rows]), bf16_bits(kc[rows]), bf16_bits(vc[rows]), lens[rows])
+    assert_close(got, want, f"decode B={B}")
+
+
 def test_decode_other_group_sizes_and_scales():
     for (Hq, Hkv, scale) in [(8, 8, None), (64, 8, None), (40, 2, None), (32, 8, 0.0), (32, 8, -0.3)]:
         _say(f"decode B=2 L=700 Hq={Hq} Hkv={Hkv} scale={scale}")
