@@ -22,8 +22,8 @@
 // has freed. The 8-wave form copies each tile once for 256 query rows instead of 128
 // and meets a barrier every other tile; with a single workgroup per CU a barrier idles
 // the whole CU, so halving them is what makes it pay (3-4% at 16K-32K keys on MI355X).
-// It needs at least 4 workgroups per CU to balance the causal triangle, so shorter
-// prompts keep the 4-wave form. Where even that grid holds at most 2 workgroups per CU,
+// With one workgroup per CU it needs enough of them to balance the causal triangle:
+// from 5/3 workgroups per CU it is the faster form, so shorter prompts keep 4 waves. Where even that grid holds at most 2 workgroups per CU,
 // the critical path is the longest query tile's walk over its keys; there a key-split
 // form (prefill_split_kernel, below) gives each 4-wave unit set a second set of 4 waves
 // that walks the other half of the key tiles. Scores are
@@ -445,11 +445,12 @@ void prefill_split_kernel(PrefillArgs a) {
 }
 
 int prefill_waves(int B, int S, int Hkv, int G) {
-  // 8 waves once their grid holds at least 4 workgroups per CU (B = 1, 32 query and 8 KV
-  // heads: S > 8128).
+  // 8 waves once their grid holds at least 5/3 workgroups per CU (B = 1, 32 query and 8
+  // KV heads: S > 3392). Paired timing on MI355X against the 4-wave form: x0.97 at 3072
+  // keys, x0.99 at 3328, x1.00 at 3456, x1.03 at 4096 and x1.04 at 8128.
   const long long units = (long long)G * ((S + 31) / 32);
   const long long wgs8 = (long long)B * Hkv * ((units + 7) / 8);
-  return wgs8 >= 4 * 256 ? 8 : 4;
+  return 3 * wgs8 >= 5 * 256 ? 8 : 4;
 }
 
 int prefill_key_splits(int B, int S, int Hkv, int G) {

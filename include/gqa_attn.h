@@ -73,10 +73,10 @@ int gqa_attn_prefill(const void* q, const void* k, const void* v, void* out,
  * waves per unit, each streaming half of them; their softmax states are merged
  * by log-sum-exp weights before the rows are written). *waves is the workgroup
  * size in waves (units x key splits) and *workgroups the size of the grid.
- * The 8-unit form is taken once its grid holds at least 4 workgroups per CU;
+ * The 8-unit form is taken once its grid holds at least 5/3 workgroups per CU;
  * the key split when the 4-unit grid holds at most 2 per CU and S >= 512.
  * For B = 1 with 32 query and 8 KV heads: S < 512 gives (4, 1),
- * 512 <= S <= 2048 gives (8, 2), S <= 8128 gives (4, 1), larger S (8, 1) as
+ * 512 <= S <= 2048 gives (8, 2), S <= 3392 gives (4, 1), larger S (8, 1) as
  * (waves, key_splits). Any output may be NULL. Returns the same shape errors
  * as gqa_attn_prefill.
  */

@@ -151,19 +151,24 @@ def test_prefill_plan(lib):
     ks = ctypes.c_int(0)
     # batch 1, Llama-3-8B heads: (waves, key splits, units per workgroup). 4 units of one
     # wave each below 512 keys; the key split (4 units x 2 waves) up to 2048 keys, while
-    # the 4-unit grid holds at most 2 workgroups per CU; 4 units again up to 8128; then 8.
+    # the 4-unit grid holds at most 2 workgroups per CU; 4 units again up to 3392 (the
+    # 8-unit grid below 5/3 workgroups per CU); then 8.
     for S, want in ((1, (4, 1, 4)), (511, (4, 1, 4)), (512, (8, 2, 4)), (1000, (8, 2, 4)),
-                    (2048, (8, 2, 4)), (2049, (4, 1, 4)), (4096, (4, 1, 4)), (8128, (4, 1, 4)),
+                    (2048, (8, 2, 4)), (2049, (4, 1, 4)), (3392, (4, 1, 4)), (3393, (8, 1, 8)),
+                    (4096, (8, 1, 8)), (8128, (8, 1, 8)),
                     (8129, (8, 1, 8)), (8192, (8, 1, 8)), (32768, (8, 1, 8))):
         assert lib.gqa_attn_prefill_plan(1, S, 32, 8, 128, ctypes.byref(waves), ctypes.byref(wgs),
                                          ctypes.byref(ks)) == 0
         assert (waves.value, ks.value) == want[:2], S
         units = 4 * -(-S // 32)
         assert wgs.value == 8 * -(-units // want[2]), S
-    # a batch reaches 4 workgroups per CU sooner, and 2 per CU sooner
+    # a batch reaches the thresholds sooner: at S = 1000, 8 units from B = 4 (512 8-unit
+    # workgroups), 4 units at B = 3 (384 of them, and 768 4-unit ones: no key split)
     assert lib.gqa_attn_prefill_plan(8, 1000, 32, 8, 128, ctypes.byref(waves), None, ctypes.byref(ks)) == 0
     assert (waves.value, ks.value) == (8, 1)
     assert lib.gqa_attn_prefill_plan(4, 1000, 32, 8, 128, ctypes.byref(waves), None, ctypes.byref(ks)) == 0
+    assert (waves.value, ks.value) == (8, 1)
+    assert lib.gqa_attn_prefill_plan(3, 1000, 32, 8, 128, ctypes.byref(waves), None, ctypes.byref(ks)) == 0
     assert (waves.value, ks.value) == (4, 1)
     assert lib.gqa_attn_prefill_plan(2, 1000, 32, 8, 128, ctypes.byref(waves), None, ctypes.byref(ks)) == 0
     assert (waves.value, ks.value) == (8, 2)

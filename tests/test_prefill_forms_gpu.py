@@ -1,7 +1,7 @@
 """Prefill parity for the two workgroup forms beside the 4-wave one.
 
 The 8-wave form (two 32-row blocks per head, a 4-stage K/V ring published two tiles per
-barrier) is taken once its grid holds at least 4 workgroups per CU; the key-split form
+barrier) is taken once its grid holds at least 5/3 workgroups per CU; the key-split form
 (4 units of two waves each, every wave streaming half of its unit's key tiles, merged by
 log-sum-exp weights) when the 4-wave grid holds at most 2. Every case first asserts,
 through gqa.prefill_plan, that the shape really runs the form under test, then checks it
@@ -27,6 +27,7 @@ def _say(msg):
 
 # (B, S, Hq, Hkv, causal, rows sampled?)
 CASES = [
+    (1, 3500, 32, 8, True, True),       # batch 1 just past the 4-wave range, ragged tail
     (8, 1000, 32, 8, True, True),
     (8, 1000, 32, 8, False, True),
     (64, 130, 32, 8, True, False),      # ragged last tile, 5 row blocks per head
