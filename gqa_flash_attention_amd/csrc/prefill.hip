@@ -3,9 +3,9 @@
 // Implements the prefill mode of the chowfi/kernels README ("Result": process the full
 // prompt with a causal mask), with three of the ideas its "What helped most" section
 // lists, redone for CDNA4:
-//  - item 2 (GQA packing): the 4 waves of a workgroup are the query heads of one KV
-//    group (or, for other group sizes, consecutive row blocks), so each K/V tile is
-//    staged once into LDS and read by every head that shares it;
+//  - item 2 (GQA packing): the waves of a workgroup are the query heads of one KV group
+//    (or, for other group sizes, consecutive row blocks), so each K/V tile is staged
+//    once into LDS and read by every head that shares it;
 //  - item 3 (skip the masked half): a workgroup stops at the last key tile its rows can
 //    see, and a wave skips the arithmetic of tiles that lie wholly above its diagonal;
 //  - item 4 (largest blocks first): workgroup ids are mapped so the query tiles with the
@@ -22,13 +22,15 @@
 // has freed. The 8-wave form copies each tile once for 256 query rows instead of 128
 // and meets a barrier every other tile; with a single workgroup per CU a barrier idles
 // the whole CU, so halving them is what makes it pay (3-4% at 16K-32K keys on MI355X).
-// With one workgroup per CU it needs enough of them to balance the causal triangle:
-// from 5/3 workgroups per CU it is the faster form, so shorter prompts keep 4 waves. Where even that grid holds at most 2 workgroups per CU,
-// the critical path is the longest query tile's walk over its keys; there a key-split
-// form (prefill_split_kernel, below) gives each 4-wave unit set a second set of 4 waves
-// that walks the other half of the key tiles. Scores are
-// computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K from LDS is the A
-// operand, the wave's Q rows stay in registers as the B operand. In that layout each
+// With one workgroup per CU it needs enough of them to balance the causal triangle: it
+// is the faster form from 5/3 workgroups per CU, and shorter prompts keep 4 waves. Where
+// even the 4-wave grid holds at most 2 workgroups per CU, the critical path is the
+// longest query tile's walk over its keys; there a key-split form (prefill_split_kernel,
+// below) gives each set of 4 units a second set of 4 waves that walks the other half of
+// the key tiles.
+//
+// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K from LDS
+// is the A operand, the wave's Q rows stay in registers as the B operand. In that layout each
 // lane's 32 scores of a 64-key tile belong to its own query row, so the row max needs
 // only one exchange between the two wave halves. The probabilities are rounded to bf16
 // in place and fed, with no data movement, as the B operand of O^T += V^T P^T; V^T comes
