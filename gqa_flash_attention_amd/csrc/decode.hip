@@ -58,9 +58,9 @@ __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
 }
 
 // Partials cross workgroups (and XCDs, each with its own L2): they are written with
-// device-coherent stores (relaxed atomic stores at agent scope, sc1), which need no
-// write-back of the whole L2 the way a release fence does. The merging workgroup
-// invalidates its own caches once (an acquire fence) and then reads them normally.
+// device-coherent stores (relaxed atomic stores at agent scope, sc1) and read back by the
+// merging workgroup with device-coherent loads, so no fence has to write back or
+// invalidate a whole cache.
 __device__ __forceinline__ void publish(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
