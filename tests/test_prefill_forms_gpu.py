@@ -106,3 +106,26 @@ def test_prefill_key_split_matches_oracle(B, S, Hq, Hkv, causal, sampled):
         got = gpu_f64(out)
         want = oracle.prefill(bf16_bits(q), bf16_bits(k), bf16_bits(v), causal=causal)
         assert_close(got, want, f"key-split B={B} S={S} Hq={Hq} Hkv={Hkv}")
+
+
+# Every form with the scales that take the kernels' other code paths: zero and negative
+# scales (the scale is then applied to the scores before the row max) and a large one.
+FORM_SHAPES = {"4-wave": (1, 300, (4, 1)), "key-split": (1, 600, (8, 2)), "8-wave": (8, 600, (8, 1))}
+
+
+@pytest.mark.parametrize("form", sorted(FORM_SHAPES))
+@pytest.mark.parametrize("scale", [0.0, -0.0883883461356163, 0.5])
+def test_every_form_with_other_scales(form, scale):
+    B, S, want_plan = FORM_SHAPES[form]
+    waves, wgs, ks = gqa.prefill_plan(B, S, 32, 8)
+    _say(f"prefill {form} B={B} S={S} scale={scale}: plan {waves} waves, {ks} key splits")
+    assert (waves, ks) == want_plan
+    q, k, v = prefill_inputs(B, S, base=7900 + S)
+    out = gqa.prefill(dev(q), dev(k), dev(v), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(S, seed=S)
+    for b in sorted({0, B - 1}):
+        got = gpu_f64(out[b:b + 1, rows])
+        want = oracle.prefill(bf16_bits(q[b:b + 1]), bf16_bits(k[b:b + 1]), bf16_bits(v[b:b + 1]),
+                              causal=True, scale=scale, rows=rows)
+        assert_close(got, want, f"{form} scale={scale} batch element {b}")
