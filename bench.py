@@ -167,7 +167,7 @@ def run_step_timing(S, L, steps, warmup):
     return wall, pf, dc
 
 
-SWEEP_CHUNK_L = (16384, 32768, 65536)
+SWEEP_CHUNK_L = (2048, 4096, 8192, 16384, 32768, 65536)
 
 
 def chunk_candidates(L: int):
