@@ -120,6 +120,12 @@ def test_decode_ws_and_split_errors(lib):
     rc = lib.gqa_attn_decode_partials(P, P, P, P, 1, big, 32, 8, 128, 0.088, 64, P, 1 << 40, None)
     assert rc == _lib.ERR_WORKSPACE
     assert lib.gqa_attn_decode_combine(P, 1 << 40, P, 1, 32, 128, (1 << 18) + 1, None) == _lib.ERR_WORKSPACE
+    # the fused decode's grid is splits x (KV heads x head groups) workgroups in one
+    # dimension: 2^18 splits of 8192 KV heads (2^31 workgroups) is refused
+    assert lib.gqa_attn_decode_workspace_bytes(1, 1 << 24, 8192, 8192, 128, 64) == 0
+    assert lib.gqa_attn_decode_workspace_bytes(1, 1 << 24, 8192, 8192, 128, 128) > 0
+    rc = lib.gqa_attn_decode_ws(P, P, P, P, P, 1, 1 << 24, 8192, 8192, 128, 0.088, 64, P, 1 << 40, None)
+    assert rc == _lib.ERR_DIM
 
 
 def test_decode_plan_and_workspace_size(lib):
