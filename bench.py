@@ -273,7 +273,7 @@ def measured_roofs():
     ms = timed(lambda: _lib.check(lib.gqa_attn_probe_hbm_read(buf.data_ptr(), nbytes, wg, sink.data_ptr(),
                                                              sink.numel(), st.cuda_stream), "probe_hbm_read"))
     out["hbm"] = {"value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                  "method": "gqa_attn_probe_hbm_read: 2 GiB read once with 16-byte non-temporal loads, 4096x256 lanes, median of 3"}
+                  "method": "gqa_attn_probe_hbm_read: 2 GiB read once with 16-byte non-temporal loads, 4096x256 lanes, the workgroups of each XCD reading one 256-byte slice of every 2 KB row (the decode's pattern), median of 3"}
     del buf, sink
     wg, rounds = 512, 6000
     sinkf = torch.empty(wg * 256, dtype=torch.float32, device=dev)

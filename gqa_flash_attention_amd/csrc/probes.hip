@@ -8,7 +8,12 @@
 //  - hbm_read: every byte of a caller buffer read once with 16-byte non-temporal loads,
 //    the decode kernel's access width and cache policy (on MI355X non-temporal reads of
 //    a 2 GiB buffer run ~6.0 TB/s against ~5.4 for plain ones). On a buffer several times
-//    the 256 MB MALL this is the cold HBM read rate a decode can reach.
+//    the 256 MB MALL this is the cold HBM read rate a decode can reach. When the buffer
+//    is whole 2 KB rows and the workgroups a multiple of 8, the workgroups with id = x
+//    (mod 8) read the 256-byte blocks at offset 256x of every row: the decode's pattern,
+//    in which the workgroups of one XCD read one KV head's 256-byte slice of each cache
+//    row (with round-robin dispatch, id mod 8 is the XCD). On MI355X that pattern reads a
+//    2 GiB buffer at ~6.2 TB/s, ~5% faster than a plain grid-stride sweep.
 //  - mfma_bf16: v_mfma_f32_32x32x16_bf16 from registers, 2 waves per SIMD on every CU, 8
 //    independent accumulators per wave, the A and B operands drawn from 8 registers of
 //    random bf16 each in a rotating pairing, so that consecutive instructions see new
@@ -35,10 +40,30 @@ __device__ __forceinline__ __bf16 random_bf16(uint32_t key) {
   return __builtin_bit_cast(__bf16, bits);
 }
 
-__global__ __launch_bounds__(256) void probe_hbm_read_kernel(const u32x4* src, size_t n16, uint32_t* sink) {
+__global__ __launch_bounds__(256) void probe_hbm_read_kernel(const u32x4* src, size_t n16, uint32_t* sink,
+                                                             int xcd_blocks) {
   const size_t tid = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t stride = (size_t)gridDim.x * 256;
   u32x4 acc = {0, 0, 0, 0};
+  if (xcd_blocks) {
+    // n16 = 128 * rows, gridDim.x = 8 * K. Workgroup (x = id mod 8, k = id / 8) reads block
+    // x (16 chunks of 16 B) of rows 16 (k + K j) + t / 16, lane t taking chunk t mod 16.
+    const size_t rows = n16 / 128;
+    const size_t x = blockIdx.x & 7, k = blockIdx.x >> 3, K = gridDim.x >> 3;
+    const size_t step = 16 * K;
+    const size_t c = (size_t)(threadIdx.x & 15) + 16 * x;
+    size_t r = 16 * k + (threadIdx.x >> 4);
+    for (; r + 3 * step < rows; r += 4 * step) {
+      const u32x4 a = __builtin_nontemporal_load(src + r * 128 + c);
+      const u32x4 b = __builtin_nontemporal_load(src + (r + step) * 128 + c);
+      const u32x4 d = __builtin_nontemporal_load(src + (r + 2 * step) * 128 + c);
+      const u32x4 e = __builtin_nontemporal_load(src + (r + 3 * step) * 128 + c);
+      acc ^= a ^ b ^ d ^ e;
+    }
+    for (; r < rows; r += step) acc ^= __builtin_nontemporal_load(src + r * 128 + c);
+    sink[tid] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    return;
+  }
+  const size_t stride = (size_t)gridDim.x * 256;
   size_t i = tid;
   // four independent 16-byte loads in flight per lane
   for (; i + 3 * stride < n16; i += 4 * stride) {
@@ -93,8 +118,9 @@ void probe_mfma_bf16_kernel(int rounds, uint32_t seed, float* sink, uint64_t* ti
 }  // namespace
 
 int launch_probe_hbm_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t stream) {
+  const int xcd_blocks = (workgroups % 8 == 0 && bytes % 2048 == 0) ? 1 : 0;
   hipLaunchKernelGGL(probe_hbm_read_kernel, dim3(workgroups), dim3(256), 0, stream,
-                     (const u32x4*)src, bytes / 16, sink);
+                     (const u32x4*)src, bytes / 16, sink, xcd_blocks);
   return (int)hipGetLastError();
 }
 

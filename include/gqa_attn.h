@@ -186,7 +186,12 @@ int gqa_attn_decode_combine(const void* ws, size_t ws_bytes, void* out,
  * with events on `stream`); neither allocates.
  *
  * Cold HBM read rate: every byte of buf is read once with 16-byte non-temporal
- * loads (the decode kernel's width and cache policy).
+ * loads (the decode kernel's width and cache policy). If bytes is a multiple of
+ * 2048 and workgroups of 8, workgroup w reads the 256-byte blocks at offset
+ * 256 (w mod 8) of each 2 KB row, the decode's pattern at 8 KV heads of 128
+ * bf16 (lane t of workgroup w = 8k + x reads chunk t mod 16 of that block in
+ * rows 16 (k + K j) + t / 16, K = workgroups / 8); otherwise lane i of the grid
+ * reads the 16-byte chunks i, i + n, i + 2n, ... (n = 256 * workgroups).
  *   buf        : device, 16-byte aligned; bytes > 0 and a multiple of 16. A buffer
  *                several times the 256 MB MALL measures HBM, not the cache.
  *   workgroups : 1..65535 workgroups of 256 lanes (4096 suits MI355X).

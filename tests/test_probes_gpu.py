@@ -20,7 +20,28 @@ def _say(msg):
     print(f"[case] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("nbytes,wg", [(1 << 20, 64), (3 * (1 << 20) + 16 * 37, 7)])
+def _expected_sinks(chunks, wg):
+    """Per-lane XOR of the chunks each lane reads, for the two read patterns the probe's
+    header documents."""
+    n16, lanes = chunks.shape[0], wg * 256
+    want = np.zeros(lanes, dtype=np.uint32)
+    if wg % 8 == 0 and n16 % 128 == 0:
+        rows, K = n16 // 128, wg // 8
+        for w in range(wg):
+            x, k = w % 8, w // 8
+            for t in range(256):
+                r = np.arange(16 * k + t // 16, rows, 16 * K)
+                acc = np.bitwise_xor.reduce(chunks[r * 128 + 16 * x + t % 16], axis=0) if len(r) else np.zeros(4, np.uint32)
+                want[w * 256 + t] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3]
+    else:
+        for t in range(lanes):
+            acc = np.bitwise_xor.reduce(chunks[t::lanes], axis=0) if t < n16 else np.zeros(4, np.uint32)
+            want[t] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3]
+    return want
+
+
+@pytest.mark.parametrize("nbytes,wg", [(1 << 20, 64), (3 * (1 << 20) + 16 * 37, 7), (3 * (1 << 20), 24),
+                                       (1 << 20, 12)])
 def test_hbm_read_probe_visits_every_chunk_once(nbytes, wg):
     _say(f"probe_hbm_read bytes={nbytes} workgroups={wg}")
     lib = _lib.get()
@@ -34,12 +55,10 @@ def test_hbm_read_probe_visits_every_chunk_once(nbytes, wg):
     torch.cuda.synchronize()
     got = sink.cpu().numpy().view(np.uint32)
     chunks = host.reshape(-1, 4)                       # 16-byte chunks
-    n16, stride = chunks.shape[0], wg * 256
-    want = np.zeros(stride, dtype=np.uint32)
-    for t in range(stride):
-        acc = np.bitwise_xor.reduce(chunks[t::stride], axis=0) if t < n16 else np.zeros(4, np.uint32)
-        want[t] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3]
-    assert np.array_equal(got, want)
+    assert np.array_equal(got, _expected_sinks(chunks, wg))
+    # every chunk is read exactly once: the lanes' XORs combine to the XOR of the buffer
+    total = np.bitwise_xor.reduce(chunks, axis=0)
+    assert np.bitwise_xor.reduce(got) == total[0] ^ total[1] ^ total[2] ^ total[3]
 
 
 def test_mfma_probe_reports_a_plausible_clock():
