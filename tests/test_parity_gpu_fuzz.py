@@ -46,6 +46,28 @@ def test_prefill_fuzz(case):
     assert_close(gpu_f64(out), want, f"prefill fuzz {case}")
 
 
+@pytest.mark.parametrize("case", range(10))
+def test_prefill_fuzz_larger_grids(case):
+    # longer prompts and batches, which reach the 8-wave and key-split forms; sampled rows
+    rng = np.random.default_rng(7200 + case)
+    Hq, Hkv = _heads(rng)
+    B = int(rng.integers(1, 9))
+    S = int(rng.integers(400, 4100))
+    causal = bool(rng.integers(0, 4))   # mostly causal
+    scale = gqa.default_scale(D) if rng.integers(0, 3) else float(np.float32(rng.uniform(-0.3, 0.3)))
+    waves, wgs, ks = gqa.prefill_plan(B, S, Hq, Hkv)
+    _say(f"prefill fuzz (larger) {case}: B={B} S={S} Hq={Hq} Hkv={Hkv} causal={causal} scale={scale:.5f} "
+         f"plan {waves} waves x {wgs}, {ks} key splits")
+    q, k, v = prefill_inputs(B, S, Hq, Hkv, base=7200 + 10 * case)
+    out = gqa.prefill(dev(q), dev(k), dev(v), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rows = sorted(set(np.random.default_rng(case).integers(0, S, size=12).tolist()) | {0, S - 1})
+    for b in sorted({0, B - 1}):
+        want = oracle.prefill(bf16_bits(q[b:b + 1]), bf16_bits(k[b:b + 1]), bf16_bits(v[b:b + 1]),
+                              causal=causal, scale=scale, rows=rows)
+        assert_close(gpu_f64(out[b:b + 1, rows]), want, f"prefill fuzz (larger) {case}, batch element {b}")
+
+
 @pytest.mark.parametrize("case", range(12))
 def test_decode_fuzz(case):
     rng = np.random.default_rng(7300 + case)
