@@ -45,7 +45,10 @@ extern "C" {
 #define GQA_ATTN_OK               0
 #define GQA_ATTN_ERR_NULL        -1  /* a required pointer is NULL                                  */
 #define GQA_ATTN_ERR_DIM         -2  /* B, S, L, Hq or Hkv < 1; Hq % Hkv != 0; non-finite scale;
-                                        a size whose element count overflows 64-bit offsets         */
+                                        a size whose element count overflows 64-bit offsets; a
+                                        launch grid past the device limits (more than 2^31-1
+                                        workgroups, or B or Hkv x ceil(G/16) above 65535 for a
+                                        decode)                                                     */
 #define GQA_ATTN_ERR_UNSUPPORTED -3  /* D != 128, or a pointer that is not 16-byte aligned          */
 #define GQA_ATTN_ERR_HIP         -4  /* a HIP launch or allocation failed (see gqa_attn_last_error) */
 #define GQA_ATTN_ERR_WORKSPACE   -5  /* caller workspace NULL/too small, or a bad split size        */
