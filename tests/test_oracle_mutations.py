@@ -1,11 +1,13 @@
 """The oracle's pins must catch plausible mistakes.
 
 Each case copies the oracle and its pin tests into a temporary directory,
-plants one mistake in the copy's source (at every place the mutated line occurs) (a wrong KV-head map, an off-by-one at
-the causal boundary, a flipped sign, a dropped scale, a biased output, a wrong
-lens clamp, a broken combine weight, a wrong bf16 widening), runs the pins on
-the copy in a subprocess and expects them to fail. The real oracle is never
-touched.
+plants one mistake in the copy's source (at every place the mutated line occurs): a
+wrong KV-head map, an off-by-one at the causal boundary, a flipped sign, a dropped
+scale, a biased output, a wrong lens clamp, a broken combine weight, a wrong bf16
+widening, reversed key dimensions, the causal mask applied to a full prefill, values
+read from the wrong KV head, a partial's log-sum-exp in the wrong base, a split chunk
+one key short, and a softmax without its max subtraction. It runs the pins on the copy
+in a subprocess and expects them to fail. The real oracle is never touched.
 """
 
 import os
@@ -28,6 +30,11 @@ MUTATIONS = [
      "w = np.where(finite, 1.0, 0.0)"),
     ("bf16_shift", "(b.astype(np.uint32) << np.uint32(16))", "(b.astype(np.uint32) << np.uint32(15))"),
     ("decode_key_dims_reversed", "x = s * (Kb[:, g, :] @ q[b, h, :])", "x = s * (Kb[:, g, ::-1] @ q[b, h, :])"),
+    ("noncausal_treated_as_causal", "nvis = int(r.max()) + 1 if causal else S", "nvis = int(r.max()) + 1"),
+    ("value_head_shifted", "Vg = v[b, :, g, :]", "Vg = v[b, :, (g + 1) % Hkv, :]"),
+    ("lse_in_log2", "lse[b, h, c] = m + np.log(tot)", "lse[b, h, c] = m + np.log2(tot)"),
+    ("chunk_end_short", "j0, j1 = c * chunk, min((c + 1) * chunk, n)", "j0, j1 = c * chunk, min((c + 1) * chunk - 1, n)"),
+    ("max_not_subtracted", "e = np.exp(x - m)", "e = np.exp(x)"),
 ]
 
 
