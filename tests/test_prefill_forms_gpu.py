@@ -129,3 +129,27 @@ def test_every_form_with_other_scales(form, scale):
         want = oracle.prefill(bf16_bits(q[b:b + 1]), bf16_bits(k[b:b + 1]), bf16_bits(v[b:b + 1]),
                               causal=True, scale=scale, rows=rows)
         assert_close(got, want, f"{form} scale={scale} batch element {b}")
+
+
+def test_8wave_form_with_idle_waves():
+    # S = 1 at B = 64: 8-wave workgroups whose second row block does not exist, so waves
+    # 4-7 stream no tile of their own; a single key must still give V[0] exactly
+    B = 64
+    assert gqa.prefill_plan(B, 1, 32, 8)[0] == 8
+    _say(f"prefill 8-wave B={B} S=1: out == V[0] bitwise")
+    q, k, v = prefill_inputs(B, 1, base=7950, sigma_qk=16.0)
+    out = gqa.prefill(dev(q), dev(k), dev(v))
+    torch.cuda.synchronize()
+    want = v.repeat_interleave(4, dim=2)          # query head h reads KV head h // 4
+    assert torch.equal(out.cpu().view(torch.int16), want.view(torch.int16))
+    # S = 40: a partial second row block and a ragged single tile
+    B, S = 64, 40
+    assert gqa.prefill_plan(B, S, 32, 8)[0] == 8
+    _say(f"prefill 8-wave B={B} S={S} against the oracle")
+    q, k, v = prefill_inputs(B, S, base=7951)
+    out = gqa.prefill(dev(q), dev(k), dev(v))
+    torch.cuda.synchronize()
+    for b in (0, B - 1):
+        got = gpu_f64(out[b:b + 1])
+        want = oracle.prefill(bf16_bits(q[b:b + 1]), bf16_bits(k[b:b + 1]), bf16_bits(v[b:b + 1]), causal=True)
+        assert_close(got, want, f"8-wave B={B} S={S} batch element {b}")
