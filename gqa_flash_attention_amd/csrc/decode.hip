@@ -91,12 +91,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;      // query head (within the served group) of this lane
   const int grp = lane >> 4;    // which 4 of the wave's 16 keys this lane scores
-  // The fused decode numbers its workgroups with the (KV head, head group) slot fastest:
-  // with round-robin dispatch over the 8 XCDs and 8 KV heads, each XCD then streams one
-  // KV head (3.5% faster at 64K keys on MI355X than interleaving the heads over the XCDs).
+  // Workgroups are numbered with the (KV head, head group) slot fastest: with round-robin
+  // dispatch over the 8 XCDs and 8 KV heads, each XCD then streams one KV head (3.5%
+  // faster at 64K keys on MI355X than interleaving the heads over the XCDs).
   const int hgs = a.Hkv * a.hgroups;
-  const int split = FUSE ? (int)(blockIdx.x / hgs) : (int)blockIdx.x;
-  const int gy = FUSE ? (int)(blockIdx.x % hgs) : (int)blockIdx.y;
+  const int split = (int)(blockIdx.x / hgs);
+  const int gy = (int)(blockIdx.x % hgs);
   const int g = gy / a.hgroups;
   const int hg = gy % a.hgroups;
   const int b = blockIdx.z;
@@ -455,13 +455,9 @@ int decode_default_chunk(int B, int L, int Hkv, int G) {
 }
 
 int launch_decode(const DecodeArgs& a, bool fused, hipStream_t stream) {
-  if (fused) {
-    const dim3 grid((unsigned)(a.nsplit * a.Hkv * a.hgroups), 1, (unsigned)a.B);
-    hipLaunchKernelGGL((decode_kernel<4, true, true>), grid, dim3(256), 0, stream, a);
-  } else {
-    const dim3 grid((unsigned)a.nsplit, (unsigned)(a.Hkv * a.hgroups), (unsigned)a.B);
-    hipLaunchKernelGGL((decode_kernel<4, false, false>), grid, dim3(256), 0, stream, a);
-  }
+  const dim3 grid((unsigned)(a.nsplit * a.Hkv * a.hgroups), 1, (unsigned)a.B);
+  if (fused) hipLaunchKernelGGL((decode_kernel<4, true, true>), grid, dim3(256), 0, stream, a);
+  else       hipLaunchKernelGGL((decode_kernel<4, false, false>), grid, dim3(256), 0, stream, a);
   return (int)hipGetLastError();
 }
 

@@ -68,7 +68,7 @@ DecodeShapeCheck check_decode_shape(int B, int L, int Hq, int Hkv, int D, float 
   r.chunk = chunk;
   const long long nsplit = ((long long)L + chunk - 1) / chunk;
   if (nsplit > gqa::kMaxSplits) { r.code = GQA_ATTN_ERR_WORKSPACE; return r; }
-  // the fused decode's grid has nsplit * Hkv * hgroups workgroups in one dimension
+  // the decode grid has nsplit * Hkv * hgroups workgroups in one dimension
   if (nsplit * Hkv * r.hgroups > 0x7fffffffLL) { r.code = GQA_ATTN_ERR_DIM; return r; }
   r.nsplit = (int)nsplit;
   if (elems4(B, Hq, r.nsplit) < 0) { r.code = GQA_ATTN_ERR_DIM; return r; }
