@@ -241,6 +241,16 @@ def sweep_chunks(path: str, rounds: int = 8):
             torch.cuda.empty_cache()
 
 
+PROBE_HBM_BYTES = 2 << 30                  # 8x the MALL
+PROBE_HBM_WORKGROUPS = 4096
+PROBE_MFMA_WORKGROUPS, PROBE_MFMA_ROUNDS = 512, 6000
+
+
+def probe_mfma_flops() -> float:
+    """FLOPs of one MFMA probe call: workgroups x 4 waves x rounds x 64 MFMAs x 32768."""
+    return float(PROBE_MFMA_WORKGROUPS * 4 * PROBE_MFMA_ROUNDS * 64 * 32768)
+
+
 def measured_roofs():
     """Run the library's two roofline probes (gqa_attn_probe_*): the cold HBM read rate
     over a 2 GiB buffer (8x the MALL) and the register-resident bf16 MFMA rate with random
@@ -266,16 +276,16 @@ def measured_roofs():
             ts.append(e0.elapsed_time(e1))
         return sorted(ts)[len(ts) // 2]
 
-    nbytes = 2 << 30
+    nbytes = PROBE_HBM_BYTES
     buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
-    wg = 4096
+    wg = PROBE_HBM_WORKGROUPS
     sink = torch.empty(wg * 256, dtype=torch.int32, device=dev)
     ms = timed(lambda: _lib.check(lib.gqa_attn_probe_hbm_read(buf.data_ptr(), nbytes, wg, sink.data_ptr(),
                                                              sink.numel(), st.cuda_stream), "probe_hbm_read"))
     out["hbm"] = {"value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                   "method": "gqa_attn_probe_hbm_read: 2 GiB read once with 16-byte non-temporal loads, 4096x256 lanes, the workgroups of each XCD reading one 256-byte slice of every 2 KB row (the decode's pattern), median of 3"}
     del buf, sink
-    wg, rounds = 512, 6000
+    wg, rounds = PROBE_MFMA_WORKGROUPS, PROBE_MFMA_ROUNDS
     sinkf = torch.empty(wg * 256, dtype=torch.float32, device=dev)
     ticks = torch.zeros(2 * wg, dtype=torch.int64, device=dev)
     ms = timed(lambda: _lib.check(lib.gqa_attn_probe_mfma_bf16(rounds, 12345, wg, sinkf.data_ptr(), sinkf.numel(),
@@ -283,7 +293,7 @@ def measured_roofs():
                                   "probe_mfma_bf16"))
     t = ticks.cpu().view(-1, 2).double()
     ghz = float((t[:, 0] / t[:, 1]).mean()) * 0.1
-    flops = wg * 4 * rounds * 64 * 32768
+    flops = probe_mfma_flops()
     out["mfma_bf16"] = {"value": round(flops / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "clock_ghz": round(ghz, 3),
                         "method": "gqa_attn_probe_mfma_bf16: v_mfma_f32_32x32x16_bf16 from registers, random bf16, "
                                   "2 waves/SIMD on every CU, median of 3"}

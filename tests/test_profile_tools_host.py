@@ -1,8 +1,10 @@
-"""The two counter post-processors on synthetic rocprofv3 output (CPU only): the per-launch
-HBM bytes of traffic.py and the clock / MFMA utilisation / FLOP ratio / hit rate of
-counters.py are recomputed here from values chosen so every figure is known in advance."""
+"""The profile post-processors on synthetic rocprofv3 output (CPU only): the per-launch HBM
+bytes of traffic.py, the clock / MFMA utilisation / FLOP ratio / hit rate of counters.py and
+the rates of kernel_stats.py are recomputed here from values chosen so every figure is known
+in advance."""
 
 import csv
+import json
 import os
 
 import pytest
@@ -101,3 +103,31 @@ def test_counters_clock_utilisation_and_flop_ratio(tmp_path):
     assert d["lds_bank_conflict_per_lds_cycle"] == pytest.approx(0.25)
     assert d["l2_hit_rate"] == pytest.approx(0.01)
     assert d["duration_us"] == pytest.approx(40.0)
+
+
+def test_kernel_stats_summary_rates(tmp_path):
+    from gqa_flash_attention_amd import kernel_stats
+    d = tmp_path / "prof"
+    d.mkdir()
+    stats = [("void gqa::prefill_kernel<true, true, 8>(gqa::PrefillArgs)", 30, 7.5e6),
+             ("gqa::probe_mfma_bf16_kernel(int)", 4, 1.45e7),
+             ("void gqa::decode_kernel<4, true, true>(gqa::DecodeArgs)", 30, 5.0e4),
+             ("gqa::probe_hbm_read_kernel(int)", 4, 3.6e5)]
+    with open(d / "bench_kernel_stats.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"])
+        w.writeheader()
+        for name, calls, ns in stats:
+            w.writerow({"Name": name, "Calls": calls, "AverageNs": ns, "MinNs": int(ns), "MaxNs": int(ns), "Percentage": 1.0})
+    S, L = 32768, 65536
+    bj = {"value": 1180.0, "config": {"prefill_S": S, "decode_L": L},
+          "prefill": {"ms": 7.45, "flops": bench.prefill_flops(S)},
+          "decode": {"ms": 0.052, "value": 5160.0, "bytes": bench.decode_bytes(L)},
+          "roofline": {"measured_peak": {"value": 1800.0, "clock_ghz": 1.8}},
+          "roofline_decode": {"measured_peak": {"value": 6200.0}}}
+    (tmp_path / "bench.json").write_text(json.dumps(bj))
+    text = kernel_stats.summarize(str(d), str(tmp_path / "bench.json"), str(tmp_path / "out.md"))
+    # rates from the averages: prefill 8.796e12 flop / 7.5 ms, decode 268.45 MB / 50 us
+    assert f"prefill {bench.prefill_flops(S) / 7.5e6 / 1e3:.0f} TFLOP/s" in text
+    assert f"decode {bench.decode_bytes(L) / 5.0e4:.0f} GB/s" in text
+    assert f"MFMA probe {bench.probe_mfma_flops() / 1.45e7 / 1e3:.0f} TFLOP/s" in text
+    assert (tmp_path / "out.md").read_text() == text
