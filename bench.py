@@ -15,7 +15,8 @@ Printed (rank 0, one JSON line): the contract fields, with
   both also carry measured_peak / frac_of_measured: the same kernel against the rate
   the library's own probes reach on this board (cold 16-byte HBM reads; register-resident
   bf16 MFMA with random operands, with the clock it ran at), taken after the timed steps;
-- cpu_baseline: the fp64 CPU oracle on a bounded sample of the same prefill.
+- cpu_baseline: the fp64 CPU oracle on a bounded sample of the same prefill;
+  cpu_baseline_decode: the same oracle on the whole decode.
 Kernel durations come from HIP events recorded on the stream the kernels run on,
 inside the timed region. The prefill streams ~671 MB between decodes, which flushes
 the 256 MB MALL, so every decode reads its cache from HBM.
@@ -132,6 +133,29 @@ def cpu_baseline(S: int, budget_s: float = 15.0):
         "sample": (f"fp64 numpy oracle, causal prefill S={S} B=1 Hq={HQ} Hkv={HKV} D={D}: "
                    f"{rows_done} query rows (all heads) in 256-row blocks spread over the sequence, "
                    f"{flops / 1e9:.1f} GFLOP algorithmic in {spent:.1f} s"),
+    }
+
+
+def cpu_baseline_decode(L: int, budget_s: float = 4.0):
+    """Time the fp64 oracle on the whole batch-1 decode against an L-token cache, repeated
+    until about budget_s seconds have been spent; reported as algorithmic GB/s."""
+    import oracle
+    from gqa_inputs import bf16_bits, decode_inputs, seed_base
+    qd, kc, vc, lens = decode_inputs(1, L, base=seed_base(1, 5))
+    qb, kb, vb = bf16_bits(qd), bf16_bits(kc), bf16_bits(vc)
+    ln = lens.numpy()
+    calls, spent = 0, 0.0
+    while spent < budget_s or calls == 0:
+        t0 = time.perf_counter()
+        oracle.decode(qb, kb, vb, ln)
+        spent += time.perf_counter() - t0
+        calls += 1
+    return {
+        "value": decode_bytes(L) * calls / spent / 1e9,
+        "unit": "GB/s",
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle, whole decode B=1 L={L} Hq={HQ} Hkv={HKV} D={D}: "
+                   f"{calls} calls in {spent:.1f} s"),
     }
 
 
@@ -370,6 +394,8 @@ def main_line(args):
         line["roofline_decode"]["frac_of_measured"] = round(dec_gbs / roofs["hbm"]["value"], 4)
     if args.cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(S, budget_s=args.cpu_budget)
+        line["cpu_baseline_decode"] = cpu_baseline_decode(L)
+        line["cpu_baseline_decode"]["cores"] = line["cpu_baseline"]["cores"]
     if args.calib_copy_mb:
         calibration_copy(args.calib_copy_mb)
     print(json.dumps(line), flush=True)
