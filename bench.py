@@ -24,6 +24,7 @@ the 256 MB MALL, so every decode reads its cache from HBM.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-probes]
     python bench.py --sweep out.jsonl     # every prefill/decode size, one JSON line each
     python bench.py --sweep-chunks out.jsonl   # decode split sizes, paired timing
+    python bench.py --sweep-forms out.jsonl    # prefill workgroup forms, paired timing
 """
 
 from __future__ import annotations
@@ -262,6 +263,56 @@ def sweep_chunks(path: str, rounds: int = 8):
                 print(json.dumps(row), flush=True)
                 f.write(json.dumps(row) + "\n")
             del kcs, vcs, wss
+            torch.cuda.empty_cache()
+
+
+SWEEP_FORM_S = (512, 1024, 2048, 3072, 4096, 8192, 16384, 32768)
+
+
+def sweep_forms(path: str, rounds: int = 8):
+    """Prefill workgroup-form sweep at B = 1 (SWEEP_FORM_S, causal): every form of
+    gqa.PREFILL_FORMS timed in paired rounds (the forms alternate in rotated order, ~0.2 s
+    of calls per form first so the clock settles), median time per form and the median of
+    per-round ratios against the form the library picks. Parity of every point against
+    the oracle is checked by tests/test_sweep_points_gpu.py on the same seeded inputs."""
+    import statistics
+    import torch
+    import gqa_flash_attention_amd as gqa
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    forms = list(gqa.PREFILL_FORMS)
+    with open(path, "w") as f:
+        for S in SWEEP_FORM_S:
+            q, k, v = make_inputs(S, 64, dev)[:3]
+            waves, _, ks = gqa.prefill_plan(1, S, 32, 8)
+            chosen = (waves, ks)
+            out = torch.empty_like(q)
+            per = prefill_flops(S) / 1.0e15            # seconds per call at ~1 PFLOP/s
+            reps = max(2, min(400, int(0.05 / per)))
+            for fm in forms:
+                for _ in range(max(3, min(4000, int(0.2 / per)))):
+                    gqa.prefill(q, k, v, out=out, form=fm)
+            torch.cuda.synchronize()
+            times = {fm: [] for fm in forms}
+            for r in range(rounds):
+                for fm in forms[r % len(forms):] + forms[:r % len(forms)]:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(st)
+                    for _ in range(reps):
+                        gqa.prefill(q, k, v, out=out, form=fm)
+                    e1.record(st)
+                    torch.cuda.synchronize()
+                    times[fm].append(e0.elapsed_time(e1) / reps)
+            for fm in forms:
+                t = statistics.median(times[fm])
+                ratio = statistics.median(times[chosen][i] / times[fm][i] for i in range(rounds))
+                row = {"mode": "prefill_form", "S": S, "waves": fm[0], "key_splits": fm[1],
+                       "chosen": fm == chosen, "status": "run", "ms_median": round(t, 5),
+                       "TFLOPs": round(prefill_flops(S) / (t * 1e-3) / 1e12, 1),
+                       "speed_vs_chosen": round(ratio, 3)}
+                print(json.dumps(row), flush=True)
+                f.write(json.dumps(row) + "\n")
+            del q, k, v, out
             torch.cuda.empty_cache()
 
 
@@ -543,6 +594,8 @@ def main():
     ap.add_argument("--sweep", metavar="OUT_JSONL", default=None)
     ap.add_argument("--sweep-chunks", metavar="OUT_JSONL", default=None,
                     help="decode split-size sweep with paired timing (see sweep_chunks)")
+    ap.add_argument("--sweep-forms", metavar="OUT_JSONL", default=None,
+                    help="prefill workgroup-form sweep with paired timing (see sweep_forms)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, one device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -558,6 +611,8 @@ def main():
         sweep(args.sweep, args.steps, args.warmup)
     elif args.sweep_chunks:
         sweep_chunks(args.sweep_chunks)
+    elif args.sweep_forms:
+        sweep_forms(args.sweep_forms)
     else:
         main_line(args)
 

@@ -62,8 +62,13 @@ def _check_bf16(name: str, t: torch.Tensor, ndim: int, device=None) -> None:
 
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
-            scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Attention over a prompt. q [B,S,Hq,D], k/v [B,S,Hkv,D] -> out [B,S,Hq,D] (bf16)."""
+            scale: float | None = None, out: torch.Tensor | None = None,
+            form: tuple[int, int] | None = None) -> torch.Tensor:
+    """Attention over a prompt. q [B,S,Hq,D], k/v [B,S,Hkv,D] -> out [B,S,Hq,D] (bf16).
+
+    ``form`` = (waves, key_splits), one of the pairs prefill_plan reports ((4, 1), (8, 1)
+    or (8, 2)), runs that workgroup form whatever the shape; None lets the library choose.
+    """
     _check_bf16("q", q, 4)
     _check_bf16("k", k, 4, q.device)
     _check_bf16("v", v, 4, q.device)
@@ -80,9 +85,15 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Tr
     if scale is None:
         scale = default_scale(D)
     with torch.cuda.device(q.device):
-        rc = _lib.get().gqa_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                         B, S, Hq, Hkv, D, float(scale), 1 if causal else 0, _stream_ptr(q))
-    _lib.check(rc, "gqa_attn_prefill")
+        if form is None:
+            rc = _lib.get().gqa_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                             B, S, Hq, Hkv, D, float(scale), 1 if causal else 0, _stream_ptr(q))
+        else:
+            waves, ks = (int(x) for x in form)
+            rc = _lib.get().gqa_attn_prefill_form(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                                  B, S, Hq, Hkv, D, float(scale), 1 if causal else 0,
+                                                  waves, ks, _stream_ptr(q))
+    _lib.check(rc, "gqa_attn_prefill_form" if form is not None else "gqa_attn_prefill")
     return out
 
 
@@ -139,6 +150,11 @@ def decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, lens: to
                                     workspace.data_ptr(), workspace.numel(), _stream_ptr(q))
     _lib.check(rc, "gqa_attn_decode_ws")
     return out
+
+
+# The workgroup forms of the prefill as (waves, key_splits): 4 units of one wave, 8 units of one
+# wave, 4 units of two waves that split the key tiles.
+PREFILL_FORMS = ((4, 1), (8, 1), (8, 2))
 
 
 def prefill_plan(B: int, S: int, Hq: int, Hkv: int, D: int = D_SUPPORTED):

@@ -28,6 +28,8 @@ _ptr = ctypes.c_void_p
 SIGNATURES = {
     "gqa_attn_prefill": (_c_int, [_ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
                                   _c_float, _c_int, _ptr]),
+    "gqa_attn_prefill_form": (_c_int, [_ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_float, _c_int, _c_int, _c_int, _ptr]),
     "gqa_attn_prefill_plan": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int,
                                        ctypes.POINTER(_c_int), ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
     "gqa_attn_decode": (_c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,

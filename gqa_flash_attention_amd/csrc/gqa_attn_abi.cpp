@@ -209,7 +209,10 @@ int gqa_attn_probe_mfma_bf16(int rounds, uint32_t seed, int workgroups,
 }
 
 // Shape checks and launch plan of a prefill (everything but the pointers).
-int plan_prefill(int B, int S, int Hq, int Hkv, int D, float scale, gqa::PrefillArgs* a) {
+// form_waves / form_ks: 0 / 0 for the library's choice, else one of the (waves, key
+// splits) pairs gqa_attn_prefill_plan reports: (4, 1), (8, 1) or (8, 2).
+int plan_prefill(int B, int S, int Hq, int Hkv, int D, float scale, gqa::PrefillArgs* a,
+                 int form_waves = 0, int form_ks = 0) {
   if (B < 1 || S < 1) return GQA_ATTN_ERR_DIM;
   int e = check_heads(Hq, Hkv, D, scale);
   if (e) return e;
@@ -217,8 +220,18 @@ int plan_prefill(int B, int S, int Hq, int Hkv, int D, float scale, gqa::Prefill
   a->B = B; a->S = S; a->Hq = Hq; a->Hkv = Hkv; a->G = Hq / Hkv;
   a->nrb = (S + 31) / 32;
   const long long units = (long long)a->G * a->nrb;
-  a->nw = gqa::prefill_waves(B, S, Hkv, a->G);
-  a->ks = gqa::prefill_key_splits(B, S, Hkv, a->G);
+  if (form_waves == 0 && form_ks == 0) {
+    a->nw = gqa::prefill_waves(B, S, Hkv, a->G);
+    a->ks = gqa::prefill_key_splits(B, S, Hkv, a->G);
+  } else if (form_waves == 4 && form_ks == 1) {
+    a->nw = 4; a->ks = 1;
+  } else if (form_waves == 8 && form_ks == 1) {
+    a->nw = 8; a->ks = 1;
+  } else if (form_waves == 8 && form_ks == 2) {
+    a->nw = 4; a->ks = 2;        // 4 units per workgroup, two waves each
+  } else {
+    return GQA_ATTN_ERR_UNSUPPORTED;
+  }
   const long long wgs = (units + a->nw - 1) / a->nw;
   const long long grid = wgs * (long long)B * Hkv;
   if (grid > 0x7fffffffLL) return GQA_ATTN_ERR_DIM;
@@ -231,9 +244,15 @@ int plan_prefill(int B, int S, int Hq, int Hkv, int D, float scale, gqa::Prefill
 int gqa_attn_prefill(const void* q, const void* k, const void* v, void* out,
                      int B, int S, int Hq, int Hkv, int D, float scale, int causal,
                      void* stream) {
+  return gqa_attn_prefill_form(q, k, v, out, B, S, Hq, Hkv, D, scale, causal, 0, 0, stream);
+}
+
+int gqa_attn_prefill_form(const void* q, const void* k, const void* v, void* out,
+                          int B, int S, int Hq, int Hkv, int D, float scale, int causal,
+                          int waves, int key_splits, void* stream) {
   if (!q || !k || !v || !out) return GQA_ATTN_ERR_NULL;
   gqa::PrefillArgs a;
-  int e = plan_prefill(B, S, Hq, Hkv, D, scale, &a);
+  int e = plan_prefill(B, S, Hq, Hkv, D, scale, &a, waves, key_splits);
   if (e) return e;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ATTN_ERR_UNSUPPORTED;
   a.q = (const uint16_t*)q;

@@ -87,6 +87,23 @@ int gqa_attn_prefill_plan(int B, int S, int Hq, int Hkv, int D, int* waves, int*
                           int* key_splits);
 
 /*
+ * gqa_attn_prefill with the workgroup form fixed by the caller instead of chosen by
+ * shape: (waves, key_splits) is one of the pairs gqa_attn_prefill_plan reports,
+ * (4, 1), (8, 1) or (8, 2), or (0, 0) for the library's choice (then the call is
+ * gqa_attn_prefill). Any other pair returns GQA_ATTN_ERR_UNSUPPORTED before any HIP
+ * call. Every form computes the same attention: (4, 1) and (8, 1) give each wave the
+ * same rows and operation order, so their outputs are identical bit for bit; (8, 2)
+ * sums each row's two key halves in another order (differences of bf16 rounding
+ * only). It exists for the sweep of tile shapes (every arrangement timed against
+ * the others in paired rounds: "Field note 005", "The loop") and for callers that
+ * want one form for every shape. Same arguments, layout, errors and asynchrony as
+ * gqa_attn_prefill; allocates nothing.
+ */
+int gqa_attn_prefill_form(const void* q, const void* k, const void* v, void* out,
+                          int B, int S, int Hq, int Hkv, int D, float scale, int causal,
+                          int waves, int key_splits, void* stream);
+
+/*
  * One-token decode against a KV cache, split along the cache.
  *   q, out         : [B, Hq, D]  bf16
  *   kcache, vcache : [B, L, Hkv, D] bf16; L is the capacity (the row stride).

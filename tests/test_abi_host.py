@@ -13,6 +13,7 @@ import re
 import pytest
 
 from gqa_flash_attention_amd import _lib
+import gqa_flash_attention_amd as gqa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
@@ -71,6 +72,19 @@ def test_prefill_argument_errors(lib):
     assert _prefill(lib, o=MIS) == _lib.ERR_UNSUPPORTED
     # element counts past 2^62 are refused rather than wrapped
     assert _prefill(lib, B=2 ** 30, S=2 ** 30) == _lib.ERR_DIM
+
+
+def test_prefill_form_argument_errors(lib):
+    def form(waves, ks, q=P, B=1, S=16, D=128):
+        return lib.gqa_attn_prefill_form(q, P, P, P, B, S, 32, 8, D, 0.088, 1, waves, ks, None)
+    # only the three forms prefill_plan reports, or (0, 0) for the library's choice
+    for waves, ks in ((4, 2), (8, 3), (12, 1), (16, 1), (2, 1), (0, 1), (4, 0), (-4, 1), (1, 1), (8, 0)):
+        assert form(waves, ks) == _lib.ERR_UNSUPPORTED, (waves, ks)
+    assert form(4, 1, q=None) == _lib.ERR_NULL
+    assert form(8, 2, B=0) == _lib.ERR_DIM
+    assert form(8, 1, D=64) == _lib.ERR_UNSUPPORTED
+    assert form(4, 1, q=MIS) == _lib.ERR_UNSUPPORTED
+    assert gqa.PREFILL_FORMS == ((4, 1), (8, 1), (8, 2))
 
 
 def _decode(lib, q=P, k=P, v=P, lens=P, o=P, B=1, L=64, Hq=32, Hkv=8, D=128, scale=0.088):

@@ -153,3 +153,35 @@ def test_8wave_form_with_idle_waves():
         got = gpu_f64(out[b:b + 1])
         want = oracle.prefill(bf16_bits(q[b:b + 1]), bf16_bits(k[b:b + 1]), bf16_bits(v[b:b + 1]), causal=True)
         assert_close(got, want, f"8-wave B={B} S={S} batch element {b}")
+
+
+# Every form at shapes the library would not pick it for (through gqa_attn_prefill_form):
+# short and long prompts, ragged tails, batches, non-causal, other head groupings.
+# (B, S, Hq, Hkv, causal)
+FORM_CASES = [
+    (1, 100, 32, 8, True),       # one key tile per unit: the key split's second half is empty
+    (1, 700, 32, 8, True),
+    (1, 4200, 32, 8, True),      # the key split where the library runs 8 waves
+    (2, 1500, 32, 8, False),
+    (3, 333, 8, 8, True),        # G = 1
+    (2, 900, 48, 8, True),       # G = 6
+]
+
+
+@pytest.mark.parametrize("form", gqa.PREFILL_FORMS)
+@pytest.mark.parametrize("B,S,Hq,Hkv,causal", FORM_CASES)
+def test_every_form_at_shapes_it_is_not_chosen_for(form, B, S, Hq, Hkv, causal):
+    _say(f"prefill form={form} B={B} S={S} Hq={Hq} Hkv={Hkv} causal={causal}; plan {gqa.prefill_plan(B, S, Hq, Hkv)}")
+    q, k, v = prefill_inputs(B, S, Hq, Hkv, D, base=7900 + B + S + Hq)
+    out = gqa.prefill(dev(q), dev(k), dev(v), causal=causal, form=form)
+    torch.cuda.synchronize()
+    rows = sample_rows(S, seed=S + B) if S > 1024 else None
+    for b in range(B):
+        got = gpu_f64(out[b:b + 1] if rows is None else out[b:b + 1, rows])
+        want = oracle.prefill(bf16_bits(q[b:b + 1]), bf16_bits(k[b:b + 1]), bf16_bits(v[b:b + 1]),
+                              causal=causal, rows=rows)
+        assert_close(got, want, f"form={form} B={B} S={S} Hq={Hq} Hkv={Hkv} batch element {b}")
+    if form == (8, 1):
+        ref = gqa.prefill(dev(q), dev(k), dev(v), causal=causal, form=(4, 1))
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)

@@ -1,5 +1,6 @@
-"""Parity of every point of the decode split-size sweep (bench.py --sweep-chunks):
-the same seeded inputs the bench uses, each runnable chunk, against the oracle."""
+"""Parity of every point of the two sweeps, on the same seeded inputs the bench uses:
+each runnable chunk of the decode split-size sweep (bench.py --sweep-chunks) and each
+workgroup form of the prefill form sweep (bench.py --sweep-forms), against the oracle."""
 
 import pytest
 import torch
@@ -8,7 +9,7 @@ import bench
 import gqa_flash_attention_amd as gqa
 import oracle
 from gqa_inputs import bf16_bits
-from parity_util import assert_close, gpu_f64
+from parity_util import assert_close, gpu_f64, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -24,3 +25,21 @@ def test_every_sweep_chunk_matches_oracle(L):
         out = gqa.decode(qd, kc, vc, lens, chunk=c)
         torch.cuda.synchronize()
         assert_close(gpu_f64(out), want, f"decode L={L} chunk={c}")
+
+
+@pytest.mark.parametrize("S", bench.SWEEP_FORM_S)
+def test_every_sweep_form_matches_oracle(S):
+    d = torch.device("cuda:0")
+    print(f"[case] sweep points prefill S={S}: forms {gqa.PREFILL_FORMS}, plan {gqa.prefill_plan(1, S, 32, 8)}",
+          flush=True)
+    q, k, v = bench.make_inputs(S, 64, d)[:3]
+    rows = sample_rows(S, seed=S)
+    want = oracle.prefill(bf16_bits(q), bf16_bits(k), bf16_bits(v), causal=True, rows=rows)
+    outs = {}
+    for fm in gqa.PREFILL_FORMS:
+        outs[fm] = gqa.prefill(q, k, v, form=fm)
+        torch.cuda.synchronize()
+        assert_close(gpu_f64(outs[fm][:, rows]), want, f"prefill S={S} form={fm}")
+    # the one-wave-per-unit forms give each wave the same rows and operation order
+    assert torch.equal(outs[(4, 1)], outs[(8, 1)])
+    assert torch.equal(gqa.prefill(q, k, v), outs[gqa.prefill_plan(1, S, 32, 8)[::2]])
