@@ -555,6 +555,27 @@ def sweep(path, steps, warmup):
         rows.append(r)
         del graph, kcs, vcs, ws, outs
         torch.cuda.empty_cache()
+    # batched decodes, every sequence at the full cache length (B*L = 256K-512K keys), caches
+    # rotated over >= 1 GB so every call reads from HBM
+    for B, L in ((32, 16384), (16, 32768), (8, 65536), (64, 4096)):
+        per = B * L * HKV * D * 2 * 2
+        ncopies = max(2, min(16, -(-(1 << 30) // per)))
+        qd = randn_bf16_device((B, HQ, D), seed_base(4, 4), dev)
+        kcs = [randn_bf16_device((B, L, HKV, D), seed_base(4, 4) + 10 + i, dev) for i in range(ncopies)]
+        vcs = [randn_bf16_device((B, L, HKV, D), seed_base(4, 4) + 30 + i, dev) for i in range(ncopies)]
+        lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+        out = torch.empty_like(qd)
+        call = lambda i: gqa.decode(qd, kcs[i % ncopies], vcs[i % ncopies], lens, out=out)
+        n = settle(call, max(warmup, ncopies))
+        ms = timed(call, max(steps, n))
+        med = ms[len(ms) // 2]
+        r = {"mode": "decode_batched", "B": B, "L": L, "ms_median": med, "ms_min": ms[0],
+             "copies_rotated": ncopies, "gbs": decode_bytes(B * L, B) / (med * 1e-3) / 1e9}
+        r["frac_of_peak"] = r["gbs"] / PEAK_HBM_GBS
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+        del kcs, vcs
+        torch.cuda.empty_cache()
     # the ragged batch: B = 16, capacity 50001, lengths U[1, 50001] (the parity tests' seed);
     # each cache copy is 3.3 GB, so every call reads cold from HBM
     B, L = 16, 50001

@@ -101,3 +101,25 @@ def test_decode_largest_batch():
         assert_close(gpu_f64(out[b:b + 1]), want, f"decode B={B}, sequence {b} (lens {lens_h[b]})")
     del kc, vc
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B,L", [(32, 16384), (16, 32768), (8, 65536), (64, 4096)])
+def test_decode_batched_full_length_sampled_sequences(B, L):
+    """The batched decodes bench.py --sweep times (same shapes, same device generator and
+    seeds as its first cache copy): every sequence at the full cache length, sampled
+    sequences against the oracle."""
+    from gqa_inputs import seed_base
+    _say(f"decode batched B={B} L={L}, plan {gqa.decode_plan(B, L, 32, 8)}: sampled sequences")
+    d = torch.device("cuda:0")
+    q = randn_bf16_device((B, 32, D), seed_base(4, 4), d)
+    kc = randn_bf16_device((B, L, 8, D), seed_base(4, 4) + 10, d)
+    vc = randn_bf16_device((B, L, 8, D), seed_base(4, 4) + 30, d)
+    lens = torch.full((B,), L, dtype=torch.int32, device=d)
+    out = gqa.decode(q, kc, vc, lens)
+    torch.cuda.synchronize()
+    for b in sorted({0, 1, B // 2, B - 1}):
+        want = oracle.decode(bf16_bits(q[b:b + 1]), bf16_bits(kc[b:b + 1]), bf16_bits(vc[b:b + 1]),
+                             np.array([L], dtype=np.int32))
+        assert_close(gpu_f64(out[b:b + 1]), want, f"decode B={B} L={L}, sequence {b}")
+    del kc, vc
+    torch.cuda.empty_cache()
