@@ -317,7 +317,7 @@ def sweep_forms(path: str, rounds: int = 8):
 
 
 PROBE_HBM_BYTES = 2 << 30                  # 8x the MALL
-PROBE_HBM_WORKGROUPS = 4096
+PROBE_HBM_WORKGROUPS = 512               # 2 per CU: the fastest count measured (256-32768)
 PROBE_MFMA_WORKGROUPS, PROBE_MFMA_ROUNDS = 512, 6000
 
 
@@ -358,7 +358,7 @@ def measured_roofs():
     ms = timed(lambda: _lib.check(lib.gqa_attn_probe_hbm_read(buf.data_ptr(), nbytes, wg, sink.data_ptr(),
                                                              sink.numel(), st.cuda_stream), "probe_hbm_read"))
     out["hbm"] = {"value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                  "method": "gqa_attn_probe_hbm_read: 2 GiB read once with 16-byte non-temporal loads, 4096x256 lanes, the workgroups of each XCD reading one 256-byte slice of every 2 KB row (the decode's pattern), median of 3"}
+                  "method": f"gqa_attn_probe_hbm_read: 2 GiB read once with 16-byte non-temporal loads, {wg}x256 lanes, the workgroups of each XCD reading one 256-byte slice of every 2 KB row (the decode's pattern), median of 3"}
     del buf, sink
     wg, rounds = PROBE_MFMA_WORKGROUPS, PROBE_MFMA_ROUNDS
     sinkf = torch.empty(wg * 256, dtype=torch.float32, device=dev)

@@ -13,7 +13,8 @@
 //    (mod 8) read the 256-byte blocks at offset 256x of every row: the decode's pattern,
 //    in which the workgroups of one XCD read one KV head's 256-byte slice of each cache
 //    row (with round-robin dispatch, id mod 8 is the XCD). On MI355X that pattern reads a
-//    2 GiB buffer at ~6.2 TB/s, ~5% faster than a plain grid-stride sweep.
+//    2 GiB buffer at ~6.6-6.8 TB/s with 512 workgroups (2 per CU, long streams per lane;
+//    ~6.2 with 1024-8192, 5.75 with 32768), ~5% faster than a plain grid-stride sweep.
 //  - mfma_bf16: v_mfma_f32_32x32x16_bf16 from registers, 2 waves per SIMD on every CU, 8
 //    independent accumulators per wave, the A and B operands drawn from 8 registers of
 //    random bf16 each in a rotating pairing, so that consecutive instructions see new

@@ -41,7 +41,7 @@ def _expected_sinks(chunks, wg):
 
 
 @pytest.mark.parametrize("nbytes,wg", [(1 << 20, 64), (3 * (1 << 20) + 16 * 37, 7), (3 * (1 << 20), 24),
-                                       (1 << 20, 12)])
+                                       (1 << 20, 12), (16 << 20, 512)])   # the last: bench.py's workgroup count
 def test_hbm_read_probe_visits_every_chunk_once(nbytes, wg):
     _say(f"probe_hbm_read bytes={nbytes} workgroups={wg}")
     lib = _lib.get()
