@@ -1,5 +1,6 @@
 """Host-side checks of bench.py (no GPU needed): the workload's work formulas, the decode
-split-sweep points, and the single-GPU guard of the command line."""
+split-sweep points, the form-sweep sizes, the decode CPU baseline's record, and the
+single-GPU guard of the command line."""
 
 import os
 import subprocess
@@ -42,3 +43,20 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_form_sweep_covers_every_plan_boundary():
+    # every workload prefill size, plus sizes on each side of the form boundaries (2048 | 2049,
+    # 3392 | 3393 at batch 1) so each form is timed where the library picks it
+    assert set(bench.SWEEP_FORM_S) >= {512, 2048, 4096, 8192, 16384, 32768}
+    assert any(512 <= S <= 2048 for S in bench.SWEEP_FORM_S)
+    assert any(2048 < S <= 3392 for S in bench.SWEEP_FORM_S)
+    assert any(S > 3392 for S in bench.SWEEP_FORM_S)
+
+
+def test_cpu_baseline_decode_record():
+    r = bench.cpu_baseline_decode(256, budget_s=0.05)
+    assert r["unit"] == "GB/s" and r["kind"] == "oracle" and r["value"] > 0
+    calls = int(r["sample"].split(": ")[1].split(" calls")[0])
+    assert calls >= 1
+    assert "L=256" in r["sample"]
