@@ -83,6 +83,33 @@ def load_traffic(kernel_key: str):
     return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
+KERNEL_TIME_FILE = os.path.join(ROOT, "profiles", "kernel_time.json")
+
+
+def load_kernel_time(key: str):
+    """Per-size kernel time (rocprofv3 trace of `--kernel-sizes`) if taken on the current sources."""
+    try:
+        with open(KERNEL_TIME_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_digest") != kernel_sources_digest():
+        return None
+    return t.get("sizes", {}).get(key)
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def make_inputs(S: int, L: int, dev):
     import torch
     from gqa_inputs import decode_inputs, prefill_inputs, seed_base
@@ -139,25 +166,40 @@ def cpu_baseline(S: int, budget_s: float = 15.0):
 
 def cpu_baseline_decode(L: int, budget_s: float = 4.0):
     """Time the fp64 oracle on the whole batch-1 decode against an L-token cache, repeated
-    until about budget_s seconds have been spent; reported as algorithmic GB/s."""
+    until about budget_s seconds have been spent; reported as algorithmic GB/s, with the
+    same measure on one BLAS thread beside it."""
     import oracle
     from gqa_inputs import bf16_bits, decode_inputs, seed_base
     qd, kc, vc, lens = decode_inputs(1, L, base=seed_base(1, 5))
     qb, kb, vb = bf16_bits(qd), bf16_bits(kc), bf16_bits(vc)
     ln = lens.numpy()
-    calls, spent = 0, 0.0
-    while spent < budget_s or calls == 0:
-        t0 = time.perf_counter()
-        oracle.decode(qb, kb, vb, ln)
-        spent += time.perf_counter() - t0
-        calls += 1
-    return {
+
+    def timed(budget):
+        calls, spent = 0, 0.0
+        while spent < budget or calls == 0:
+            t0 = time.perf_counter()
+            oracle.decode(qb, kb, vb, ln)
+            spent += time.perf_counter() - t0
+            calls += 1
+        return calls, spent
+
+    calls, spent = timed(budget_s)
+    r = {
         "value": decode_bytes(L) * calls / spent / 1e9,
         "unit": "GB/s",
         "kind": "oracle",
         "sample": (f"fp64 numpy oracle, whole decode B=1 L={L} Hq={HQ} Hkv={HKV} D={D}: "
                    f"{calls} calls in {spent:.1f} s"),
     }
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            c1, s1 = timed(budget_s / 2)
+        r["one_thread"] = {"value": decode_bytes(L) * c1 / s1 / 1e9, "unit": "GB/s", "cores": 1,
+                           "sample": f"same decode on one BLAS thread: {c1} calls in {s1:.1f} s"}
+    except Exception as e:  # threadpoolctl missing or unable to limit this BLAS
+        r["one_thread"] = {"value": None, "reason": f"BLAS threads not limitable here: {e}"}
+    return r
 
 
 def run_step_timing(S, L, steps, warmup):
@@ -232,7 +274,7 @@ def sweep_chunks(path: str, rounds: int = 8):
             kcs = [kc.clone() for _ in range(nc)]
             vcs = [vc.clone() for _ in range(nc)]
             out = torch.empty_like(qd)
-            wss = {c: torch.zeros(gqa.decode_workspace_bytes(1, L, 32, 8, 128, c), dtype=torch.uint8, device=dev)
+            wss = {c: gqa.decode_workspace(1, L, 32, 8, 128, c, device=dev)
                    for c in run}
             call = lambda c, i: gqa.decode(qd, kcs[i % nc], vcs[i % nc], lens, out=out, chunk=c, workspace=wss[c])
             for c in run:
@@ -393,6 +435,9 @@ def main_line(args):
     wall, pf, dc = run_step_timing(S, L, args.steps, args.warmup)
     pf_mean = sum(pf) / len(pf)
     dc_mean = sum(dc) / len(dc)
+
+    def pct(xs, p):
+        return xs[min(len(xs) - 1, int(p * (len(xs) - 1)))]
     fl = prefill_flops(S)
     by = decode_bytes(L)
     value = fl / (pf_mean * 1e-3) / 1e12
@@ -417,10 +462,12 @@ def main_line(args):
         "decode": {
             "value": round(dec_gbs, 1), "unit": "GB/s",
             "ms": round(dc_mean, 5), "ms_min": round(dc[0], 5), "ms_median": round(dc[len(dc) // 2], 5),
+            "ms_p05": round(pct(dc, 0.05), 5), "ms_p95": round(pct(dc, 0.95), 5),
             "bytes": by,
         },
         "prefill": {
             "ms": round(pf_mean, 4), "ms_min": round(pf[0], 4), "ms_median": round(pf[len(pf) // 2], 4),
+            "ms_p05": round(pct(pf, 0.05), 4), "ms_p95": round(pct(pf, 0.95), 4),
             "flops": fl,
         },
         "roofline": {
@@ -436,7 +483,19 @@ def main_line(args):
             "kernel": "decode_kernel<fused> (split-KV + in-kernel merge, one launch)",
         },
         "device": torch.cuda.get_device_name(0),
+        "host_cpu": host_cpu_model(),
     }
+    # Kernel time (rocprofv3 trace of `--kernel-sizes` on the same kernel sources): the
+    # dispatch's own duration, without the launch gap the per-call events above include.
+    for obj, key, work, unit, peak in ((line["roofline"], f"prefill_S{S}", fl, 1e12, PEAK_BF16_TFLOPS),
+                                       (line["roofline_decode"], f"decode_L{L}", by, 1e9, PEAK_HBM_GBS)):
+        kt = load_kernel_time(key)
+        if kt is not None:
+            rate = work / (kt["kernel_us_median"] * 1e-6) / unit
+            obj["kernel_time"] = {"us_median": round(kt["kernel_us_median"], 2),
+                                  "us_p05": round(kt["kernel_us_p05"], 2), "us_p95": round(kt["kernel_us_p95"], 2),
+                                  "achieved": round(rate, 1), "frac": round(rate / peak, 4),
+                                  "source": "profiles/kernel_time.json"}
     if args.probes:
         roofs = measured_roofs()
         line["roofline"]["measured_peak"] = roofs["mfma_bf16"]
@@ -447,6 +506,7 @@ def main_line(args):
         line["cpu_baseline"] = cpu_baseline(S, budget_s=args.cpu_budget)
         line["cpu_baseline_decode"] = cpu_baseline_decode(L)
         line["cpu_baseline_decode"]["cores"] = line["cpu_baseline"]["cores"]
+        line["cpu_baseline"]["cpu_model"] = line["host_cpu"]
     if args.calib_copy_mb:
         calibration_copy(args.calib_copy_mb)
     print(json.dumps(line), flush=True)
@@ -530,7 +590,7 @@ def sweep(path, steps, warmup):
         qd, lens = qd.to(dev), lens.to(dev)
         kcs = [kc.to(dev) for _ in range(ncopies)]
         vcs = [vc.to(dev) for _ in range(ncopies)]
-        ws = torch.zeros(gqa.decode_workspace_bytes(1, L, HQ, HKV, D), dtype=torch.uint8, device=dev)
+        ws = gqa.decode_workspace(1, L, HQ, HKV, D, device=dev)
         outs = [torch.empty_like(qd) for _ in range(16)]
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -601,6 +661,68 @@ def sweep(path, steps, warmup):
             f.write(json.dumps(r) + "\n")
 
 
+KERNEL_SIZES_PREFILL = (2048, 4096, 8192, 16384, 32768)
+KERNEL_SIZES_DECODE = (2048, 4096, 8192, 16384, 32768, 65536)
+
+
+def kernel_sizes(path: str, timed: int = 200):
+    """Every prefill and decode size of the workload (B = 1), one after another, for a
+    rocprofv3 kernel trace: per size a fixed number of settling calls (~0.2 s) and then
+    `timed` calls, each between HIP events on the kernels' stream. Decode caches rotate
+    through >= 1 GB of copies, so no call finds its cache in the MALL. One JSON line per
+    size records the call counts (kernel_stats.py --sizes matches them, in order, with the
+    trace's dispatches) and the event figures. Run it under
+        rocprofv3 --kernel-trace --output-format csv -d DIR -o sizes -- python3 bench.py --kernel-sizes OUT
+    and summarize with python -m gqa_flash_attention_amd.kernel_stats --sizes DIR OUT."""
+    import statistics
+    import torch
+    import gqa_flash_attention_amd as gqa
+    from gqa_inputs import decode_inputs, prefill_inputs, seed_base
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    rows = []
+
+    def run(kind, size, call, per_call_ms, extra):
+        settle = max(5, min(5000, int(200.0 / per_call_ms)))
+        for i in range(settle):
+            call(i)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(timed)]
+        for i in range(timed):
+            evs[i][0].record(st)
+            call(settle + i)
+            evs[i][1].record(st)
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)
+        r = {"mode": kind, ("S" if kind == "prefill" else "L"): size, "settle_calls": settle, "timed_calls": timed,
+             "event_ms_median": statistics.median(ms), "event_ms_p05": ms[int(0.05 * (timed - 1))],
+             "event_ms_p95": ms[int(0.95 * (timed - 1))], "event_ms_min": ms[0], **extra}
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+
+    for S in KERNEL_SIZES_PREFILL:
+        q, k, v = [x.to(dev) for x in prefill_inputs(1, S, base=seed_base(2, KERNEL_SIZES_PREFILL.index(S)))]
+        out = torch.empty_like(q)
+        run("prefill", S, lambda i: gqa.prefill(q, k, v, out=out), prefill_flops(S) / 1.0e12,
+            {"flops": prefill_flops(S)})
+        del q, k, v, out
+    for L in KERNEL_SIZES_DECODE:
+        per = L * HKV * D * 2 * 2
+        nc = max(2, min(64, -(-(1 << 30) // per)))
+        qd, kc, vc, lens = decode_inputs(1, L, base=seed_base(1, KERNEL_SIZES_DECODE.index(L)))
+        qd, lens = qd.to(dev), lens.to(dev)
+        kcs = [kc.to(dev) for _ in range(nc)]
+        vcs = [vc.to(dev) for _ in range(nc)]
+        out = torch.empty_like(qd)
+        run("decode", L, lambda i: gqa.decode(qd, kcs[i % nc], vcs[i % nc], lens, out=out), 0.02,
+            {"bytes": decode_bytes(L), "copies_rotated": nc})
+        del kcs, vcs
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        for r in rows:
+            f.write(json.dumps(r) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -617,6 +739,8 @@ def main():
                     help="decode split-size sweep with paired timing (see sweep_chunks)")
     ap.add_argument("--sweep-forms", metavar="OUT_JSONL", default=None,
                     help="prefill workgroup-form sweep with paired timing (see sweep_forms)")
+    ap.add_argument("--kernel-sizes", metavar="OUT_JSONL", default=None,
+                    help="every prefill/decode size back to back, for a rocprofv3 kernel trace (see kernel_sizes)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, one device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -634,6 +758,8 @@ def main():
         sweep_chunks(args.sweep_chunks)
     elif args.sweep_forms:
         sweep_forms(args.sweep_forms)
+    elif args.kernel_sizes:
+        kernel_sizes(args.kernel_sizes)
     else:
         main_line(args)
 

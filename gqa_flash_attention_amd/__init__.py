@@ -19,8 +19,8 @@ from . import _lib
 from ._lib import GqaAttnError  # noqa: F401
 
 __all__ = [
-    "prefill", "prefill_plan", "decode", "decode_plan", "decode_workspace_bytes", "decode_partials",
-    "decode_combine", "default_scale", "release", "version", "GqaAttnError",
+    "prefill", "prefill_plan", "decode", "decode_plan", "decode_workspace_bytes", "decode_workspace",
+    "decode_partials", "decode_combine", "default_scale", "release", "version", "GqaAttnError",
 ]
 
 D_SUPPORTED = 128
@@ -118,9 +118,9 @@ def decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, lens: to
 
     With neither ``chunk`` nor ``workspace`` the library picks the split and uses
     its own cached workspace; otherwise a torch-owned workspace is used (allocated
-    here, zeroed, if not given) with the requested keys per split. A workspace
-    passed in must have been allocated zeroed (its leading merge counters must be
-    zero; every completed call leaves them zero).
+    and zeroed here if not given) with the requested keys per split. A workspace
+    passed in must have been allocated zeroed (decode_workspace() returns one): its
+    leading merge counters must be zero, and every completed call leaves them zero.
     """
     B, L, Hq, Hkv, D = _check_decode(q, kcache, vcache, lens)
     if out is None:
@@ -141,10 +141,8 @@ def decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, lens: to
             _lib.check(rc, "gqa_attn_decode")
             return out
         ch = 0 if chunk is None else int(chunk)
-        need = lib.gqa_attn_decode_workspace_bytes(B, L, Hq, Hkv, D, ch)
         if workspace is None:
-            # zeroed: the merge counters at the start of the workspace must start at zero
-            workspace = torch.zeros(max(int(need), 16), dtype=torch.uint8, device=q.device)
+            workspace = decode_workspace(B, L, Hq, Hkv, D, ch, device=q.device)
         rc = lib.gqa_attn_decode_ws(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), lens.data_ptr(),
                                     out.data_ptr(), B, L, Hq, Hkv, D, float(scale), ch,
                                     workspace.data_ptr(), workspace.numel(), _stream_ptr(q))
@@ -179,6 +177,17 @@ def decode_plan(B: int, L: int, Hq: int, Hkv: int, D: int = D_SUPPORTED):
 
 def decode_workspace_bytes(B: int, L: int, Hq: int, Hkv: int, D: int = D_SUPPORTED, chunk: int = 0) -> int:
     return int(_lib.get().gqa_attn_decode_workspace_bytes(B, L, Hq, Hkv, D, chunk))
+
+
+def decode_workspace(B: int, L: int, Hq: int, Hkv: int, D: int = D_SUPPORTED, chunk: int = 0,
+                     device=None) -> torch.Tensor:
+    """A zeroed workspace for decodes of this shape with `chunk` keys per split (0 = the
+    library's choice), allocated by torch on `device` (default: the current GPU)."""
+    need = int(_lib.get().gqa_attn_decode_workspace_bytes(B, L, Hq, Hkv, D, int(chunk)))
+    if need == 0:
+        raise GqaAttnError(_lib.ERR_WORKSPACE, "gqa_attn_decode_workspace_bytes")
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    return torch.zeros(need, dtype=torch.uint8, device=dev)
 
 
 def _split_views(ws: torch.Tensor, B: int, Hq: int, nsplit: int, D: int):

@@ -287,12 +287,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   if (!FUSE || a.nsplit == 1) return;
 
-  // Count this split. The partial was written with device-coherent stores, and the
-  // barrier below waits for them to complete (vmcnt(0)) before the count, so when the
-  // last workgroup's count returns, every split's partial is in memory. That workgroup
-  // merges them, reading with device-coherent loads (which cannot hit a stale line in
-  // its XCD's L2, so no cache-wide invalidation is needed), and afterwards resets the
-  // counter for the next call. No workgroup ever waits for another.
+  // Count this split, in this order:
+  //  1. each thread waits until its own partial stores have completed (vmcnt(0): a
+  //     device-coherent store counts as completed once it is visible at agent scope);
+  //  2. the barrier then tells thread 0 that every thread of the workgroup got there;
+  //  3. only then does thread 0 count the split.
+  // So when the last workgroup's count returns, every split's partial is in memory. That
+  // workgroup merges them, reading with device-coherent loads (which cannot hit a stale
+  // line in its XCD's L2, so no cache-wide invalidation is needed), and afterwards resets
+  // the counter for the next call. No workgroup ever waits for another. The wait in 1 is
+  // explicit, not left to how the barrier's own fence happens to be lowered.
+  wait_vmcnt<0>();
   __syncthreads();
   int* counter = a.counters + (size_t)b * a.Hkv * a.hgroups + gy;
   if (threadIdx.x == 0)
@@ -467,16 +472,17 @@ int launch_decode_combine(const CombineArgs& a, hipStream_t stream) {
   return (int)hipGetLastError();
 }
 
-// Clears the merge counters of a new workspace. A kernel rather than hipMemsetAsync so
-// that a caller may capture the first decode on a stream into a HIP graph.
-__global__ __launch_bounds__(256) void zero_words_kernel(int* p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0;
+// Fills a new workspace's merge counters (with zero). A kernel rather than
+// hipMemsetAsync so that a caller may capture the first decode on a stream into a HIP graph.
+__global__ __launch_bounds__(256) void fill_words_kernel(uint32_t* p, size_t n, uint32_t value) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = value;
 }
 
-int launch_zero_words(int* p, size_t n, hipStream_t stream) {
+int launch_fill_words(uint32_t* p, size_t n, uint32_t value, hipStream_t stream) {
   if (n == 0) return 0;
   const size_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream, p, n);
+  hipLaunchKernelGGL(fill_words_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream, p, n,
+                     value);
   return (int)hipGetLastError();
 }
 

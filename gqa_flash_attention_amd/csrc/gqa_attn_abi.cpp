@@ -12,6 +12,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "gqa_internal.hpp"
 
@@ -94,42 +95,40 @@ WsLayout ws_layout(int B, int Hq, int nsplit) {
 }
 size_t ws_bytes_for(int B, int Hq, int nsplit) { return ws_layout(B, Hq, nsplit).total; }
 
-// Library-owned decode workspaces, one per (device, stream), grown on demand.
+// Library-owned decode workspaces, one per (device, stream), grown on demand. A buffer
+// that has been handed to a launch is never freed before gqa_attn_release: when a larger
+// one replaces it, it moves to the retired list, because earlier launches on the stream,
+// or a HIP graph captured from one, may still use it.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
-  size_t zero_counters = 0;   // leading int32 counters known to be zero
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, void*>, Workspace> g_ws;
+std::vector<std::pair<int, void*>> g_retired;   // (device, buffer)
 
-int get_workspace(size_t need, size_t counters, hipStream_t stream, void** out) {
+// With g_ws_mutex held by the caller (until its launch has been enqueued, so that no
+// other thread can retire the buffer in between).
+int get_workspace(size_t need, hipStream_t stream, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail("hipGetDevice", e);
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
   Workspace& w = g_ws[{dev, (void*)stream}];
   if (w.bytes < need) {
-    if (w.ptr) {
-      // Earlier decodes on this stream may still read the old buffer.
-      e = hipStreamSynchronize(stream);
-      if (e != hipSuccess) return hip_fail("hipStreamSynchronize", e);
-      e = hipFree(w.ptr);
-      w.ptr = nullptr;
-      w.bytes = 0;
-      w.zero_counters = 0;
-      if (e != hipSuccess) return hip_fail("hipFree", e);
-    }
     const size_t grow = (need + (1u << 20) - 1) / (1u << 20) * (1u << 20);
-    e = hipMalloc(&w.ptr, grow);
-    if (e != hipSuccess) { w.ptr = nullptr; return hip_fail("hipMalloc(decode workspace)", e); }
+    void* p = nullptr;
+    e = hipMalloc(&p, grow);
+    if (e != hipSuccess) return hip_fail("hipMalloc(decode workspace)", e);
+    // The merge counters must start at zero (every completed decode leaves them zero):
+    // cleared on the stream, ahead of the launch that will use the buffer.
+    const int fe = gqa::launch_fill_words((uint32_t*)p, grow / 4, 0u, stream);
+    if (fe != 0) {
+      (void)hipFree(p);
+      return hip_fail("fill_words launch (decode workspace)", fe);
+    }
+    if (w.ptr) g_retired.emplace_back(dev, w.ptr);
+    w.ptr = p;
     w.bytes = grow;
-  }
-  if (w.zero_counters < counters) {
-    // The merge counters must start at zero; every completed decode leaves them zero.
-    const int ze = gqa::launch_zero_words((int*)w.ptr, counters, stream);
-    if (ze != 0) return hip_fail("zero_words launch (decode counters)", ze);
-    w.zero_counters = counters;
   }
   *out = w.ptr;
   return 0;
@@ -217,9 +216,16 @@ int plan_prefill(int B, int S, int Hq, int Hkv, int D, float scale, gqa::Prefill
   int e = check_heads(Hq, Hkv, D, scale);
   if (e) return e;
   if (elems4(B, S, Hq) < 0) return GQA_ATTN_ERR_DIM;
+  // The copies of a full K/V tile address row r (r < 64) of the tile with the 32-bit
+  // per-lane byte offset r * Hkv * 256 + (chunk slot) * 16; refuse head counts for which
+  // that offset would wrap (Hkv >= 266306) instead of reading other rows.
+  if ((long long)(gqa::kTileRowsHost - 1) * Hkv * gqa::kRowBytesHost + (gqa::kRowBytesHost - 1) >= (1LL << 32))
+    return GQA_ATTN_ERR_DIM;
   a->B = B; a->S = S; a->Hq = Hq; a->Hkv = Hkv; a->G = Hq / Hkv;
   a->nrb = (S + 31) / 32;
   const long long units = (long long)a->G * a->nrb;
+  // unit indices (workgroup * waves + wave) are 32-bit in the kernels
+  if (units > 0x7fffffffLL - 16) return GQA_ATTN_ERR_DIM;
   if (form_waves == 0 && form_ks == 0) {
     a->nw = gqa::prefill_waves(B, S, Hkv, a->G);
     a->ks = gqa::prefill_key_splits(B, S, Hkv, a->G);
@@ -300,7 +306,8 @@ int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
     return GQA_ATTN_ERR_UNSUPPORTED;
   void* ws = nullptr;
   const WsLayout w = ws_layout(B, Hq, s.nsplit);
-  int e = get_workspace(w.total, w.cnt_count, (hipStream_t)stream, &ws);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int e = get_workspace(w.total, (hipStream_t)stream, &ws);
   if (e) return e;
   return run_decode(q, kcache, vcache, lens, out, B, L, Hq, Hkv, scale, s, ws, (hipStream_t)stream);
 }
@@ -351,7 +358,7 @@ int gqa_attn_decode_combine(const void* ws, size_t ws_bytes, void* out,
 
 void gqa_attn_release(void) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  if (g_ws.empty()) return;
+  if (g_ws.empty() && g_retired.empty()) return;
   int cur = 0;
   (void)hipGetDevice(&cur);
   for (auto& kv : g_ws) {
@@ -360,7 +367,12 @@ void gqa_attn_release(void) {
       (void)hipFree(kv.second.ptr);
     }
   }
+  for (auto& r : g_retired) {
+    (void)hipSetDevice(r.first);
+    (void)hipFree(r.second);
+  }
   g_ws.clear();
+  g_retired.clear();
   (void)hipSetDevice(cur);
 }
 

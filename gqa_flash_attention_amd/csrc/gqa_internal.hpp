@@ -54,13 +54,19 @@ int launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
 // fused = false: only the per-chunk partials (o_part, lse).
 int launch_decode(const DecodeArgs& a, bool fused, hipStream_t stream);
 int launch_decode_combine(const CombineArgs& a, hipStream_t stream);
-// Zeroes n int32 words at p (device memory) on `stream`.
-int launch_zero_words(int* p, size_t n, hipStream_t stream);
+// Fills n 32-bit words at p (device memory) with `value` on `stream` (a kernel, not a
+// memset, so that the call may be captured into a HIP graph).
+int launch_fill_words(uint32_t* p, size_t n, uint32_t value, hipStream_t stream);
 
 // Measurement probes (probes.hip).
 int launch_probe_hbm_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
 int launch_probe_mfma_bf16(int rounds, uint32_t seed, int workgroups, float* sink, uint64_t* ticks,
                            hipStream_t stream);
+
+// Rows per staged K/V tile (gqa_device.hpp's kTileRows) and bytes per bf16 row of
+// D = 128, for the host-side bounds on tile offsets.
+constexpr int kTileRowsHost = 64;
+constexpr int kRowBytesHost = 128 * 2;
 
 // Keys per split chosen for a decode of this shape (a multiple of 64).
 int decode_default_chunk(int B, int L, int Hkv, int G);

@@ -11,6 +11,15 @@ Usage (repository root, library built in-tree):
 The summary lists each kernel's dispatch count and average / min / max duration from
 `bench_kernel_stats.csv`, the rates those averages give for the prefill, the decode and the
 two probes, and beside them the bench's HIP-event figures, which hold each launch's dispatch.
+
+Per-size kernel times (every prefill and decode size of the workload):
+
+    rocprofv3 --kernel-trace --output-format csv -d <dir> -o sizes -- \
+        python3 bench.py --kernel-sizes sizes.jsonl
+    python -m gqa_flash_attention_amd.kernel_stats --sizes <dir> sizes.jsonl
+
+writes profiles/kernel_time_prefill_decode_sizes.md and profiles/kernel_time.json (with the
+digest of the kernel sources, so bench.py reports these kernel times only while they match).
 """
 
 from __future__ import annotations
@@ -20,6 +29,7 @@ import csv
 import glob
 import json
 import os
+import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -89,14 +99,114 @@ def summarize(prof_dir: str, bench_json: str, out: str) -> str:
     return text
 
 
+SIZES_CMD = ("rocprofv3 --kernel-trace --output-format csv -d <dir> -o sizes -- "
+             "python3 bench.py --kernel-sizes sizes.jsonl")
+
+
+def _trace_dispatches(prof_dir: str):
+    """[(kind, duration_ns)] of the attention kernels in dispatch order: kind 'prefill' for
+    every prefill form, 'decode' for the fused and split decode kernels."""
+    paths = glob.glob(os.path.join(prof_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_trace.csv under {prof_dir}")
+    out = []
+    for r in csv.DictReader(open(paths[0])):
+        name = r["Kernel_Name"]
+        if "prefill_kernel" in name or "prefill_split_kernel" in name:
+            kind = "prefill"
+        elif "decode_kernel" in name:
+            kind = "decode"
+        else:
+            continue
+        out.append((int(r["Start_Timestamp"]), kind, int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), name))
+    out.sort()
+    return [(k, d, n) for _, k, d, n in out]
+
+
+def _pct(xs, p):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(p * (len(xs) - 1)))]
+
+
+def summarize_sizes(prof_dir: str, sizes_jsonl: str, out_md: str, out_json: str) -> str:
+    """Per-size kernel time from a trace of `bench.py --kernel-sizes`: the dispatches of each
+    kind are taken in order, each size consuming its settling calls and then its timed calls
+    (the counts its JSON line records); statistics over the timed ones."""
+    sys.path.insert(0, ROOT)
+    import bench  # noqa: E402  (same repository: peaks, digest)
+    disp = _trace_dispatches(prof_dir)
+    rows = [json.loads(ln) for ln in open(sizes_jsonl) if ln.strip()]
+    pos = {"prefill": 0, "decode": 0}
+    by_kind = {k: [d for d in disp if d[0] == k] for k in pos}
+    res = {}
+    for r in rows:
+        kind = r["mode"]
+        n0, n1 = r["settle_calls"], r["timed_calls"]
+        seq = by_kind[kind][pos[kind]: pos[kind] + n0 + n1]
+        if len(seq) != n0 + n1:
+            raise SystemExit(f"trace holds {len(seq)} {kind} dispatches for {r}, expected {n0 + n1}")
+        pos[kind] += n0 + n1
+        ns = [d for _, d, _ in seq[n0:]]
+        names = sorted({n for _, _, n in seq[n0:]})
+        med = statistics.median(ns)
+        e = {"kernel": names, "calls": n1, "kernel_us_median": med / 1e3, "kernel_us_mean": sum(ns) / len(ns) / 1e3,
+             "kernel_us_p05": _pct(ns, 0.05) / 1e3, "kernel_us_p95": _pct(ns, 0.95) / 1e3,
+             "kernel_us_min": min(ns) / 1e3, "event_us_median": r["event_ms_median"] * 1e3,
+             "event_us_p05": r["event_ms_p05"] * 1e3, "event_us_p95": r["event_ms_p95"] * 1e3}
+        if kind == "prefill":
+            key = f"prefill_S{r['S']}"
+            e["tflops_kernel"] = r["flops"] / (med * 1e-9) / 1e12
+            e["frac_kernel"] = e["tflops_kernel"] / bench.PEAK_BF16_TFLOPS
+            e["tflops_event"] = r["flops"] / (r["event_ms_median"] * 1e-3) / 1e12
+        else:
+            key = f"decode_L{r['L']}"
+            e["gbs_kernel"] = r["bytes"] / (med * 1e-9) / 1e9
+            e["frac_kernel"] = e["gbs_kernel"] / bench.PEAK_HBM_GBS
+            e["gbs_event"] = r["bytes"] / (r["event_ms_median"] * 1e-3) / 1e9
+        res[key] = e
+    for k in pos:
+        if pos[k] != len(by_kind[k]):
+            raise SystemExit(f"{len(by_kind[k]) - pos[k]} {k} dispatches in the trace are not accounted for")
+    doc = {"sources_digest": bench.kernel_sources_digest(), "command": SIZES_CMD, "sizes": res}
+    with open(out_json, "w") as f:
+        json.dump(doc, f, indent=1)
+    lines = ["# Kernel time per workload size: causal prefill and decode, B = 1, 32 query / 8 KV heads, d = 128, bf16",
+             "", "Commands (repository root, library built in-tree beforehand with "
+             "`python -m gqa_flash_attention_amd.build`):", "", "```", "export TMPDIR=/tmp", SIZES_CMD,
+             "python -m gqa_flash_attention_amd.kernel_stats --sizes <dir> sizes.jsonl", "```", "",
+             f"Kernel sources digest `{doc['sources_digest']}`. Per size: ~0.2 s of settling calls, then the timed "
+             "calls; kernel time is each dispatch's own duration in the trace, the event span is the bench's HIP "
+             "events around each call (it also holds the dispatch). Decode caches rotate over >= 1 GB of copies, "
+             "so each decode reads from HBM. Fractions are of 2.5 PFLOP/s (bf16 dense) and 8 TB/s.", "",
+             "| size | kernel | calls | kernel us median (p05-p95) | event us median | rate by kernel time | "
+             "fraction of peak |", "|---|---|---|---|---|---|---|"]
+    for key, e in res.items():
+        rate = (f"{e['tflops_kernel']:.0f} TFLOP/s" if key.startswith("prefill")
+                else f"{e['gbs_kernel']:.0f} GB/s")
+        kn = ", ".join(f"`{n}`" for n in e["kernel"])
+        lines.append(f"| {key} | {kn} | {e['calls']} | {e['kernel_us_median']:.2f} ({e['kernel_us_p05']:.2f}-"
+                     f"{e['kernel_us_p95']:.2f}) | {e['event_us_median']:.2f} | {rate} | {e['frac_kernel']:.3f} |")
+    text = "\n".join(lines) + "\n"
+    with open(out_md, "w") as f:
+        f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("prof_dir")
-    ap.add_argument("bench_json")
-    ap.add_argument("--out", default=os.path.join(ROOT, "profiles",
-                                                  "bench_prefill_S32768_decode_L65536_kernel_stats.md"))
+    ap.add_argument("bench_json", help="the bench's JSON line, or with --sizes the --kernel-sizes JSONL")
+    ap.add_argument("--sizes", action="store_true",
+                    help="summarize a trace of `bench.py --kernel-sizes` into per-size kernel times")
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--out-json", default=os.path.join(ROOT, "profiles", "kernel_time.json"))
     a = ap.parse_args()
-    print(summarize(a.prof_dir, a.bench_json, a.out))
+    if a.sizes:
+        out = a.out or os.path.join(ROOT, "profiles", "kernel_time_prefill_decode_sizes.md")
+        print(summarize_sizes(a.prof_dir, a.bench_json, out, a.out_json))
+    else:
+        out = a.out or os.path.join(ROOT, "profiles", "bench_prefill_S32768_decode_L65536_kernel_stats.md")
+        print(summarize(a.prof_dir, a.bench_json, out))
 
 
 if __name__ == "__main__":

@@ -27,7 +27,8 @@
  *  - Arguments are validated before any HIP call, so every error code below
  *    except GQA_ATTN_ERR_HIP can be produced on a machine without a GPU.
  *  - Results are bitwise deterministic for a fixed shape, scale and split
- *    count: no reduction uses atomics.
+ *    count: no reduction uses atomics (the decode's atomic only elects the
+ *    workgroup that merges; the merge order is fixed).
  *  - Entry points may be called from several host threads. Calls that share
  *    a stream are ordered by that stream.
  */
@@ -48,7 +49,9 @@ extern "C" {
                                         a size whose element count overflows 64-bit offsets; a
                                         launch grid past the device limits (more than 2^31-1
                                         workgroups, or B or Hkv x ceil(G/16) above 65535 for a
-                                        decode)                                                     */
+                                        decode); a prefill with Hkv >= 266306 (the byte offset
+                                        63 x Hkv x 256 of a K/V tile row then passes 2^32) or
+                                        with (Hq/Hkv) x ceil(S/32) >= 2^31 - 16 row blocks     */
 #define GQA_ATTN_ERR_UNSUPPORTED -3  /* D != 128, or a pointer that is not 16-byte aligned          */
 #define GQA_ATTN_ERR_HIP         -4  /* a HIP launch or allocation failed (see gqa_attn_last_error) */
 #define GQA_ATTN_ERR_WORKSPACE   -5  /* caller workspace NULL/too small, or a bad split size        */
@@ -120,16 +123,19 @@ int gqa_attn_prefill_form(const void* q, const void* k, const void* v, void* out
  * split's K/V rows are read once, with non-temporal loads, for all query heads
  * of their group (item 2). The merge happens in the same kernel launch (item 5,
  * one fewer launch): the last workgroup to finish a (sequence, KV head) merges
- * it.
+ * it, after every other split has published its partial and counted itself.
  * The split partials live in a library-owned workspace, cached per (device,
- * stream) and grown on demand: one hipMalloc (and a clear of the new buffer's
- * counters by a small kernel) the first time a larger size is needed, none
- * afterwards. Concurrent streams never share a workspace. To capture this call
- * into a HIP graph, make one call of at least that size on the capturing
- * stream first (a capture cannot allocate), or use gqa_attn_decode_ws; the
- * graph then uses that stream's workspace wherever it is replayed, so a replay
- * must not overlap other decodes on that stream. A stream's workspace is kept
- * until gqa_attn_release, keyed by the stream handle.
+ * stream) and grown on demand: one hipMalloc (and a clear of the new buffer by a
+ * small kernel on `stream`) the first time a larger size is needed, none
+ * afterwards. Concurrent streams never share a workspace. A workspace that has
+ * been used is never freed before gqa_attn_release: when a larger one replaces
+ * it, the old one is kept (earlier work on the stream, or a graph captured from
+ * it, may still use it). To capture this call into a HIP graph, make one call
+ * of at least that size on the capturing stream first (a capture cannot
+ * allocate), or use gqa_attn_decode_ws; the graph then uses that workspace
+ * wherever it is replayed, so a replay must not overlap other decodes on that
+ * stream's workspace. Calls from several host threads are safe: the workspace
+ * of a stream is looked up, grown and launched on under one lock.
  */
 int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
                     const int32_t* lens, void* out,
@@ -244,8 +250,10 @@ const char* gqa_attn_strerror(int code);
 /* Detail of the most recent GQA_ATTN_ERR_HIP on the calling thread ("" if none). */
 const char* gqa_attn_last_error(void);
 
-/* Frees the library-cached decode workspaces. The caller must ensure no decode
- * using them is still in flight (for example by synchronising the device). */
+/* Frees the library-cached decode workspaces, including those replaced by larger
+ * ones. The caller must ensure no decode using them is still in flight (for
+ * example by synchronising the device) and that no captured graph that uses
+ * them will be replayed. */
 void gqa_attn_release(void);
 
 /* ABI version of this header. */

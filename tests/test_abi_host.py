@@ -74,6 +74,22 @@ def test_prefill_argument_errors(lib):
     assert _prefill(lib, B=2 ** 30, S=2 ** 30) == _lib.ERR_DIM
 
 
+def test_prefill_tile_offset_bound(lib):
+    # A full K/V tile is copied with 32-bit per-lane byte offsets r * Hkv * 256 + 16 * slot
+    # (r < 64, slot < 16). The largest offset is 63 * Hkv * 256 + 255: below 2^32 up to
+    # Hkv = 266305, so that head count is accepted and the next one refused (ERR_DIM, before
+    # any HIP call; the pointers are fake and never touched).
+    assert 63 * 266305 * 256 + 255 < 2 ** 32 <= 63 * 266306 * 256 + 255
+    for Hkv, want in ((266305, 0), (266306, _lib.ERR_DIM), (1 << 20, _lib.ERR_DIM), ((1 << 31) - 1, _lib.ERR_DIM)):
+        assert lib.gqa_attn_prefill_plan(1, 64, Hkv, Hkv, 128, None, None, None) == want, Hkv
+        if want:
+            assert _prefill(lib, S=64, Hq=Hkv, Hkv=Hkv) == want, Hkv
+            assert lib.gqa_attn_prefill_form(P, P, P, P, 1, 64, Hkv, Hkv, 128, 0.088, 1, 4, 1, None) == want
+    # row blocks x group size must stay below 2^31 - 16 (32-bit unit indices in the kernels)
+    assert lib.gqa_attn_prefill_plan(1, 1 << 26, 1 << 10, 1, 128, None, None, None) == _lib.ERR_DIM
+    assert lib.gqa_attn_prefill_plan(1, 1 << 20, 1 << 10, 1, 128, None, None, None) == 0
+
+
 def test_prefill_form_argument_errors(lib):
     def form(waves, ks, q=P, B=1, S=16, D=128):
         return lib.gqa_attn_prefill_form(q, P, P, P, B, S, 32, 8, D, 0.088, 1, waves, ks, None)

@@ -27,7 +27,7 @@ def test_alternating_caches_reuse_one_workspace_bitwise(B, L):
     _say(f"fused decode B={B} L={L}: two caches alternating 400 times on one workspace")
     ins = [decode_inputs(B, L, base=9500 + 10 * i + B) for i in range(2)]
     dev = [[t.to(d) for t in x] for x in ins]
-    ws = torch.zeros(gqa.decode_workspace_bytes(B, L, 32, 8, 128), dtype=torch.uint8, device=d)
+    ws = gqa.decode_workspace(B, L, 32, 8, 128, device=d)
     ref = []
     for i in range(2):
         q, kc, vc, lens = dev[i]

@@ -25,7 +25,7 @@ def test_prefill_and_decode_replay_from_a_graph():
     _say(f"graph: prefill B={B} S={S} + decode B={B} L={L}, 5 replays with new inputs")
     pq, pk, pv = [t.to(d) for t in prefill_inputs(B, S, base=9800)]
     dq, kc, vc, lens = [t.to(d) for t in decode_inputs(B, L, base=9810, lens=[L, L // 3])]
-    ws = torch.zeros(gqa.decode_workspace_bytes(B, L, 32, 8, 128), dtype=torch.uint8, device=d)
+    ws = gqa.decode_workspace(B, L, 32, 8, 128, device=d)
     pout = torch.empty_like(pq)
     dout = torch.empty_like(dq)
     # warm up on a side stream, as graph capture requires
@@ -81,3 +81,79 @@ def test_decode_on_the_library_workspace_replays_from_a_graph():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(dout, want), f"replay {r}: decode differs"
+
+
+def test_graph_replay_survives_a_larger_eager_decode_on_the_same_stream():
+    # The library workspace a graph was captured on must outlive its replacement: an eager
+    # decode that needs more workspace on the capturing stream gets a new, larger buffer,
+    # and the old one (which the graph's kernel still addresses) is kept until
+    # gqa_attn_release.
+    d = torch.device("cuda:0")
+    B, L = 1, 4096
+    _say(f"graph: decode B={B} L={L} captured on a stream's library workspace; a larger eager decode (B=64, "
+         f"L=1024: a 2 MB workspace against 1 MB) grows that workspace; 3 replays after it")
+    dq, kc, vc, lens = [t.to(d) for t in decode_inputs(B, L, base=9890)]
+    dout = torch.empty_like(dq)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gqa.decode(dq, kc, vc, lens, out=dout)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        gqa.decode(dq, kc, vc, lens, out=dout)
+    torch.cuda.synchronize()
+    bq, bkc, bvc, blens = [t.to(d) for t in decode_inputs(64, 1024, base=9895)]
+    with torch.cuda.stream(s):
+        big = gqa.decode(bq, bkc, bvc, blens)     # grows the capturing stream's workspace
+    torch.cuda.synchronize()
+    for r in range(3):
+        ndq, nkc, nvc, _ = [t.to(d) for t in decode_inputs(B, L, base=9896 + 10 * r)]
+        for dst, src in ((dq, ndq), (kc, nkc), (vc, nvc)):
+            dst.copy_(src)
+        want = gqa.decode(dq, kc, vc, lens)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dout, want), f"replay {r}: decode differs"
+    with torch.cuda.stream(s):
+        again = gqa.decode(bq, bkc, bvc, blens)
+    torch.cuda.synchronize()
+    assert torch.equal(big, again)
+
+
+def test_decodes_from_two_host_threads_on_one_stream():
+    # Both threads use the library workspace of the same stream, with shapes that make it
+    # grow; lookup, growth and launch happen under one lock, so neither thread can launch
+    # into a buffer the other has replaced. Every output must equal a single-threaded call.
+    import threading
+    d = torch.device("cuda:0")
+    shapes = [(1, 2048), (2, 8192), (64, 1024), (4, 16384)]   # (64, 1024) grows the workspace past 1 MB
+    _say(f"two host threads, one stream, decodes of shapes {shapes} in turn, 6 rounds each")
+    ins = {sh: [t.to(d) for t in decode_inputs(sh[0], sh[1], base=9990 + sh[0] + sh[1] // 1024)] for sh in shapes}
+    ref = {sh: gqa.decode(*ins[sh]) for sh in shapes}
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    outs = {0: [], 1: []}
+    errors = []
+
+    def worker(k):
+        try:
+            with torch.cuda.stream(s):
+                for r in range(6):
+                    sh = shapes[(r + 2 * k) % len(shapes)]
+                    outs[k].append((sh, gqa.decode(*ins[sh])))
+        except Exception as e:  # surfaced below
+            errors.append(e)
+
+    th = [threading.Thread(target=worker, args=(k,)) for k in (0, 1)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k in (0, 1):
+        for sh, o in outs[k]:
+            assert torch.equal(o, ref[sh]), f"thread {k} shape {sh} differs"
