@@ -19,7 +19,7 @@ from . import _lib
 from ._lib import GqaAttnError  # noqa: F401
 
 __all__ = [
-    "prefill", "prefill_plan", "decode", "decode_plan", "decode_workspace_bytes", "decode_workspace",
+    "prefill", "prefill_plan", "decode", "decode_noalloc", "decode_plan", "decode_workspace_bytes", "decode_workspace",
     "decode_partials", "decode_combine", "default_scale", "release", "version", "GqaAttnError",
 ]
 
@@ -147,6 +147,24 @@ def decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, lens: to
                                     out.data_ptr(), B, L, Hq, Hkv, D, float(scale), ch,
                                     workspace.data_ptr(), workspace.numel(), _stream_ptr(q))
     _lib.check(rc, "gqa_attn_decode_ws")
+    return out
+
+
+def decode_noalloc(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, lens: torch.Tensor,
+                   out: torch.Tensor, scale: float | None = None) -> torch.Tensor:
+    """decode() through gqa_attn_decode_noalloc: the library allocates nothing (its split
+    partials live in a fixed 8 MiB scratch per GPU, shared by every call on that GPU, so
+    overlapping calls on one GPU race). The caller passes `out` [B,Hq,D] bf16."""
+    B, L, Hq, Hkv, D = _check_decode(q, kcache, vcache, lens)
+    _check_bf16("out", out, 3, q.device)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = default_scale(D)
+    with torch.cuda.device(q.device):
+        rc = _lib.get().gqa_attn_decode_noalloc(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), lens.data_ptr(),
+                                                out.data_ptr(), B, L, Hq, Hkv, D, float(scale), _stream_ptr(q))
+    _lib.check(rc, "gqa_attn_decode_noalloc")
     return out
 
 

@@ -37,6 +37,8 @@ SIGNATURES = {
     "gqa_attn_decode_plan": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int,
                                       ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
     "gqa_attn_decode_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "gqa_attn_decode_noalloc": (_c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                         _c_float, _ptr]),
     "gqa_attn_decode_ws": (_c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     _c_float, _c_int, _ptr, _c_size_t, _ptr]),
     "gqa_attn_decode_partials": (_c_int, [_ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,

@@ -134,6 +134,39 @@ int get_workspace(size_t need, hipStream_t stream, void** out) {
   return 0;
 }
 
+// Scratch for gqa_attn_decode_noalloc: the decode workspace of callers that cannot
+// allocate. One copy per GPU (a device global lives on every device the library runs on),
+// kept until the process ends. Host code never uses the array's name as an address: the
+// per-device address comes from hipGetSymbolAddress (scratch_on_current_device).
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+struct ScratchState {
+  void* ptr = nullptr;   // the device address of `scratch` on that device
+};
+std::mutex g_scratch_mutex;
+std::map<int, ScratchState> g_scratch;
+
+// With g_scratch_mutex held: the address of the current device's scratch. The first call on
+// a device looks the address up and clears the whole array (a kernel on `stream`, so the
+// merge counters start at zero; every completed decode leaves them zero).
+int scratch_on_current_device(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  ScratchState& st = g_scratch[dev];
+  if (!st.ptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail("hipGetSymbolAddress(scratch)", e != hipSuccess ? e : hipErrorUnknown);
+    const int fe = gqa::launch_fill_words((uint32_t*)p, kScratchBytes / 4, 0u, stream);
+    if (fe != 0) return hip_fail("fill_words launch (scratch)", fe);
+    st.ptr = p;
+  }
+  *out = st.ptr;
+  return 0;
+}
+
 gqa::DecodeArgs make_decode_args(const void* q, const void* kc, const void* vc, const int32_t* lens,
                                  int B, int L, int Hq, int Hkv, float scale,
                                  const DecodeShapeCheck& s, void* ws) {
@@ -308,6 +341,30 @@ int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
   const WsLayout w = ws_layout(B, Hq, s.nsplit);
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   int e = get_workspace(w.total, (hipStream_t)stream, &ws);
+  if (e) return e;
+  return run_decode(q, kcache, vcache, lens, out, B, L, Hq, Hkv, scale, s, ws, (hipStream_t)stream);
+}
+
+int gqa_attn_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                            const int32_t* lens, void* out,
+                            int B, int L, int Hq, int Hkv, int D, float scale,
+                            void* stream) {
+  if (!q || !kcache || !vcache || !lens || !out) return GQA_ATTN_ERR_NULL;
+  DecodeShapeCheck s = check_decode_shape(B, L, Hq, Hkv, D, scale, 0);
+  if (s.code) return s.code;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out))
+    return GQA_ATTN_ERR_UNSUPPORTED;
+  const size_t need = ws_bytes_for(B, Hq, s.nsplit);
+  if (need > kScratchBytes) {
+    char buf[160];
+    std::snprintf(buf, sizeof(buf), "gqa_attn_decode_noalloc: this shape needs %zu bytes of scratch, more than the %zu "
+                  "the library holds per GPU", need, kScratchBytes);
+    g_last_error = buf;
+    return GQA_ATTN_ERR_WORKSPACE;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  void* ws = nullptr;
+  const int e = scratch_on_current_device((hipStream_t)stream, &ws);
   if (e) return e;
   return run_decode(q, kcache, vcache, lens, out, B, L, Hq, Hkv, scale, s, ws, (hipStream_t)stream);
 }

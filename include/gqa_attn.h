@@ -180,6 +180,27 @@ int gqa_attn_decode_ws(const void* q, const void* kcache, const void* vcache,
                        int chunk, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * gqa_attn_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, semantics, split and results (bit for bit) as gqa_attn_decode, but
+ * the split partials and merge counters live in a fixed 8 MiB scratch array
+ * that the library holds on each GPU until the process ends. The call
+ * allocates nothing: it makes no hipMalloc, hipFree or other allocating call.
+ * Shapes whose workspace (gqa_attn_decode_workspace_bytes with chunk 0)
+ * exceeds 8 MiB are rejected with GQA_ATTN_ERR_WORKSPACE before any HIP call,
+ * with the sizes in gqa_attn_last_error (with 32 query heads and 8 KV heads the
+ * workspace is 0.52 MiB at batch 1 for every L up to 131072 and 4.05 MiB at
+ * L = 2^20). The first call on a GPU also clears that GPU's scratch with a
+ * small kernel on `stream`. Every call on one GPU shares its scratch: calls
+ * that overlap in time on one GPU (other streams, other threads) race and must
+ * be serialised by the caller.
+ */
+int gqa_attn_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                            const int32_t* lens, void* out,
+                            int B, int L, int Hq, int Hkv, int D, float scale,
+                            void* stream);
+
+/*
  * The first half of a decode on its own: per-split partial results. Here split
  * s is the contiguous chunk of cache slots [s*chunk, (s+1)*chunk), clipped to
  * lens[b] (the fused entry points above assign keys to splits differently; their

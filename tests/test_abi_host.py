@@ -236,3 +236,21 @@ def test_probe_argument_errors(lib):
     assert lib.gqa_attn_probe_mfma_bf16(8, 1, 0, P, 1 << 17, P, 1024, None) == _lib.ERR_DIM
     assert lib.gqa_attn_probe_mfma_bf16(8, 1, 512, P, (1 << 17) - 1, P, 1024, None) == _lib.ERR_WORKSPACE
     assert lib.gqa_attn_probe_mfma_bf16(8, 1, 512, P, 1 << 17, P, 1023, None) == _lib.ERR_WORKSPACE
+
+
+def test_decode_noalloc_argument_errors(lib):
+    def call(q=P, k=P, v=P, lens=P, o=P, B=1, L=64, Hq=32, Hkv=8, D=128, scale=0.088):
+        return lib.gqa_attn_decode_noalloc(q, k, v, lens, o, B, L, Hq, Hkv, D, scale, None)
+    assert call(lens=None) == _lib.ERR_NULL
+    assert call(o=None) == _lib.ERR_NULL
+    assert call(B=0) == _lib.ERR_DIM
+    assert call(Hq=12) == _lib.ERR_DIM
+    assert call(D=64) == _lib.ERR_UNSUPPORTED
+    assert call(k=MIS) == _lib.ERR_UNSUPPORTED
+    # the per-GPU scratch holds 8 MiB: a batch-1 decode of 2^21 keys needs 8.08 MiB and is
+    # refused before any HIP call, with the sizes in the error detail
+    assert lib.gqa_attn_decode_workspace_bytes(1, 1 << 21, 32, 8, 128, 0) > 8 << 20
+    assert lib.gqa_attn_decode_workspace_bytes(1, 1 << 20, 32, 8, 128, 0) <= 8 << 20
+    assert call(L=1 << 21) == _lib.ERR_WORKSPACE
+    assert b"scratch" in lib.gqa_attn_last_error()
+    assert call(B=64, L=50000) == _lib.ERR_WORKSPACE
