@@ -28,6 +28,9 @@ namespace gqa {
 
 namespace {
 
+// An integer hash for the probe's random operands: the "lowbias32" xorshift-multiply
+// function found by Chris Wellons' hash-prospector search (two multiply constants
+// 0x7feb352d and 0x846ca68b, shifts 16/15/16), reimplemented here.
 __device__ __forceinline__ uint32_t mix32(uint32_t x) {
   x ^= x >> 16; x *= 0x7feb352dU; x ^= x >> 15; x *= 0x846ca68bU; x ^= x >> 16;
   return x;
