@@ -358,6 +358,54 @@ def sweep_forms(path: str, rounds: int = 8):
             torch.cuda.empty_cache()
 
 
+SWEEP_TILE_S = (1024, 4096, 8192, 16384, 32768)
+
+
+def sweep_tiles(path: str, rounds: int = 8):
+    """Prefill tile-shape sweep at B = 1 (SWEEP_TILE_S, causal): every shape of
+    gqa.PREFILL_TILES (rows per wave, keys per tile, waves per workgroup) timed in paired
+    rounds as in sweep_forms, against the library's own 8-wave form (32, 64, 8). Parity of
+    every point against the oracle: tests/test_sweep_points_gpu.py."""
+    import statistics
+    import torch
+    import gqa_flash_attention_amd as gqa
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    shapes = list(gqa.PREFILL_TILES)
+    ref = (32, 64, 8)
+    with open(path, "w") as f:
+        for S in SWEEP_TILE_S:
+            q, k, v = make_inputs(S, 64, dev)[:3]
+            out = torch.empty_like(q)
+            per = prefill_flops(S) / 1.0e15
+            reps = max(2, min(400, int(0.05 / per)))
+            for tl in shapes:
+                for _ in range(max(3, min(4000, int(0.2 / per)))):
+                    gqa.prefill(q, k, v, out=out, tiles=tl)
+            torch.cuda.synchronize()
+            times = {tl: [] for tl in shapes}
+            for r in range(rounds):
+                for tl in shapes[r % len(shapes):] + shapes[:r % len(shapes)]:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(st)
+                    for _ in range(reps):
+                        gqa.prefill(q, k, v, out=out, tiles=tl)
+                    e1.record(st)
+                    torch.cuda.synchronize()
+                    times[tl].append(e0.elapsed_time(e1) / reps)
+            for tl in shapes:
+                t = statistics.median(times[tl])
+                ratio = statistics.median(times[ref][i] / times[tl][i] for i in range(rounds))
+                row = {"mode": "prefill_tiles", "S": S, "rows_per_wave": tl[0], "keys_per_tile": tl[1],
+                       "waves": tl[2], "status": "run", "ms_median": round(t, 5),
+                       "TFLOPs": round(prefill_flops(S) / (t * 1e-3) / 1e12, 1),
+                       "speed_vs_32x64x8": round(ratio, 3)}
+                print(json.dumps(row), flush=True)
+                f.write(json.dumps(row) + "\n")
+            del q, k, v, out
+            torch.cuda.empty_cache()
+
+
 PROBE_HBM_BYTES = 2 << 30                  # 8x the MALL
 PROBE_HBM_WORKGROUPS = 512               # 2 per CU: the fastest count measured (256-32768)
 PROBE_MFMA_WORKGROUPS, PROBE_MFMA_ROUNDS = 512, 6000
@@ -739,6 +787,8 @@ def main():
                     help="decode split-size sweep with paired timing (see sweep_chunks)")
     ap.add_argument("--sweep-forms", metavar="OUT_JSONL", default=None,
                     help="prefill workgroup-form sweep with paired timing (see sweep_forms)")
+    ap.add_argument("--sweep-tiles", metavar="OUT_JSONL", default=None,
+                    help="prefill tile-shape sweep with paired timing (see sweep_tiles)")
     ap.add_argument("--kernel-sizes", metavar="OUT_JSONL", default=None,
                     help="every prefill/decode size back to back, for a rocprofv3 kernel trace (see kernel_sizes)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -758,6 +808,8 @@ def main():
         sweep_chunks(args.sweep_chunks)
     elif args.sweep_forms:
         sweep_forms(args.sweep_forms)
+    elif args.sweep_tiles:
+        sweep_tiles(args.sweep_tiles)
     elif args.kernel_sizes:
         kernel_sizes(args.kernel_sizes)
     else:

@@ -63,11 +63,13 @@ def _check_bf16(name: str, t: torch.Tensor, ndim: int, device=None) -> None:
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
             scale: float | None = None, out: torch.Tensor | None = None,
-            form: tuple[int, int] | None = None) -> torch.Tensor:
+            form: tuple[int, int] | None = None, tiles: tuple[int, int, int] | None = None) -> torch.Tensor:
     """Attention over a prompt. q [B,S,Hq,D], k/v [B,S,Hkv,D] -> out [B,S,Hq,D] (bf16).
 
     ``form`` = (waves, key_splits), one of the pairs prefill_plan reports ((4, 1), (8, 1)
-    or (8, 2)), runs that workgroup form whatever the shape; None lets the library choose.
+    or (8, 2)), runs that workgroup form whatever the shape; ``tiles`` =
+    (rows_per_wave, keys_per_tile, waves), one of PREFILL_TILES, runs that tile shape;
+    with neither the library chooses.
     """
     _check_bf16("q", q, 4)
     _check_bf16("k", k, 4, q.device)
@@ -84,7 +86,16 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Tr
             raise ValueError("out must have q's shape")
     if scale is None:
         scale = default_scale(D)
+    if form is not None and tiles is not None:
+        raise ValueError("give form or tiles, not both")
     with torch.cuda.device(q.device):
+        if tiles is not None:
+            bm, bn, nw = (int(x) for x in tiles)
+            rc = _lib.get().gqa_attn_prefill_tiles(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                                   B, S, Hq, Hkv, D, float(scale), 1 if causal else 0,
+                                                   bm, bn, nw, _stream_ptr(q))
+            _lib.check(rc, "gqa_attn_prefill_tiles")
+            return out
         if form is None:
             rc = _lib.get().gqa_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                              B, S, Hq, Hkv, D, float(scale), 1 if causal else 0, _stream_ptr(q))
@@ -171,6 +182,10 @@ def decode_noalloc(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, 
 # The workgroup forms of the prefill as (waves, key_splits): 4 units of one wave, 8 units of one
 # wave, 4 units of two waves that split the key tiles.
 PREFILL_FORMS = ((4, 1), (8, 1), (8, 2))
+# The tile shapes gqa_attn_prefill_tiles runs, as (rows per wave, keys per tile, waves per
+# workgroup); the first two are the library's own 4- and 8-wave forms.
+PREFILL_TILES = ((32, 64, 4), (32, 64, 8), (32, 32, 4), (32, 32, 8), (32, 128, 4), (32, 128, 8),
+                 (64, 32, 4), (64, 64, 4))
 
 
 def prefill_plan(B: int, S: int, Hq: int, Hkv: int, D: int = D_SUPPORTED):

@@ -30,6 +30,8 @@ SIGNATURES = {
                                   _c_float, _c_int, _ptr]),
     "gqa_attn_prefill_form": (_c_int, [_ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_float, _c_int, _c_int, _c_int, _ptr]),
+    "gqa_attn_prefill_tiles": (_c_int, [_ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                        _c_float, _c_int, _c_int, _c_int, _c_int, _ptr]),
     "gqa_attn_prefill_plan": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int,
                                        ctypes.POINTER(_c_int), ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
     "gqa_attn_decode": (_c_int, [_ptr, _ptr, _ptr, _ptr, _ptr, _c_int, _c_int, _c_int, _c_int, _c_int,

@@ -303,6 +303,41 @@ int gqa_attn_prefill_form(const void* q, const void* k, const void* v, void* out
   return GQA_ATTN_OK;
 }
 
+int gqa_attn_prefill_tiles(const void* q, const void* k, const void* v, void* out,
+                           int B, int S, int Hq, int Hkv, int D, float scale, int causal,
+                           int rows_per_wave, int keys_per_tile, int waves, void* stream) {
+  if (!q || !k || !v || !out) return GQA_ATTN_ERR_NULL;
+  const int key = 1000 * rows_per_wave + 10 * keys_per_tile + waves;
+  const bool product = (key == 32644 || key == 32648);   // the 4- and 8-wave forms
+  const bool sweep = (key == 32324 || key == 32328 || key == 33284 || key == 33288 || key == 64324 || key == 64644);
+  if (!product && !sweep) return GQA_ATTN_ERR_UNSUPPORTED;
+  gqa::PrefillArgs a;
+  int e = plan_prefill(B, S, Hq, Hkv, D, scale, &a, product ? waves : 4, 1);
+  if (e) return e;
+  // 128-key tiles address rows up to 127 with the same 32-bit per-lane offsets
+  if ((long long)(keys_per_tile - 1) * Hkv * gqa::kRowBytesHost + (gqa::kRowBytesHost - 1) >= (1LL << 32))
+    return GQA_ATTN_ERR_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ATTN_ERR_UNSUPPORTED;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.out = (uint16_t*)out;
+  if (product) {
+    e = gqa::launch_prefill(a, causal != 0, (hipStream_t)stream);
+  } else {
+    // units (32-row blocks of one head) per workgroup, and the grid for it
+    a.nw = waves * rows_per_wave / 32;
+    a.ks = 1;
+    const long long units = (long long)a.G * a.nrb;
+    const long long wgs = (units + a.nw - 1) / a.nw;
+    if (wgs * (long long)a.nslots > 0x7fffffffLL) return GQA_ATTN_ERR_DIM;
+    a.wgs_per_slot = (int)wgs;
+    e = gqa::launch_prefill_tiles(a, causal != 0, rows_per_wave, keys_per_tile, waves, (hipStream_t)stream);
+  }
+  if (e != 0) return hip_fail("prefill (tile form) launch", e);
+  return GQA_ATTN_OK;
+}
+
 int gqa_attn_prefill_plan(int B, int S, int Hq, int Hkv, int D, int* waves, int* workgroups,
                           int* key_splits) {
   gqa::PrefillArgs a;

@@ -50,6 +50,11 @@ struct CombineArgs {
 int prefill_waves(int B, int S, int Hkv, int G);
 int prefill_key_splits(int B, int S, int Hkv, int G);
 int launch_prefill(const PrefillArgs& a, bool causal, hipStream_t stream);
+// The prefill with another tile shape (the sweep's forms other than the 64-key, 32-row
+// ones): (rows_per_wave, keys_per_tile, waves) in {(32, 32, 4), (32, 32, 8), (32, 128, 4),
+// (32, 128, 8), (64, 32, 4), (64, 64, 4)}; a.nw must be waves * rows_per_wave / 32.
+int launch_prefill_tiles(const PrefillArgs& a, bool causal, int rows_per_wave, int keys_per_tile, int waves,
+                         hipStream_t stream);
 // fused = true: split, then merge in the last-arriving workgroup, writing `out`.
 // fused = false: only the per-chunk partials (o_part, lse).
 int launch_decode(const DecodeArgs& a, bool fused, hipStream_t stream);

@@ -446,6 +446,275 @@ void prefill_split_kernel(PrefillArgs a) {
   store_rows(a, b, qpos, head, h, l_tot, st);
 }
 
+// ----------------------------------------------------------------------------------------
+// Other tile shapes, for the tile-shape sweep (gqa_attn_prefill_tiles). The forms above use
+// 64-key tiles and 32 query rows per wave; here the key tile holds BN = 32 * NB keys
+// (NB = 1, 2 or 4 blocks of 32) and a wave owns NQ = 1 or 2 units of 32 rows (BM = 32 * NQ
+// rows per wave), with every K and V fragment read from LDS feeding the MFMAs of all NQ
+// units. The arithmetic per unit is the product's: S^T = K Q^T, base-2 online softmax with
+// the lazy rescale, bf16 P into O^T += V^T P^T. With NQ = 2 a wave carries twice the state
+// (about 300 registers) and runs alone on its SIMD.
+// ----------------------------------------------------------------------------------------
+
+// Copies of a full BN-row K/V tile, per-lane offsets computed once (as TileCopy does for
+// 64 rows): instruction j of wave w fills rows 4 (w + NW j) .. +3.
+template <int NW, int BN>
+struct TileCopyN {
+  static constexpr int kPer = (BN / 4) / NW;
+  static_assert(kPer >= 1 && (BN / 4) % NW == 0, "tile rows per wave");
+  uint32_t ko[kPer], vo[kPer];
+  __device__ __forceinline__ void init(size_t row_stride_elems, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int r = 4 * (wave + NW * j) + (lane >> 4);
+      const int slot = lane & 15;
+      const uint32_t row = (uint32_t)(r * row_stride_elems * 2);
+      ko[j] = row + (uint32_t)((slot ^ swz_k(r)) << 4);
+      vo[j] = row + (uint32_t)((slot ^ swz_v(r)) << 4);
+    }
+  }
+  __device__ __forceinline__ void issue_full(GQA_LDS uint8_t* kt, GQA_LDS uint8_t* vt, const uint16_t* kg,
+                                             const uint16_t* vg, int wave) const {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) lds_dma16_sv(kg, ko[j], kt + (wave + NW * j) * 1024);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) lds_dma16_sv(vg, vo[j], vt + (wave + NW * j) * 1024);
+  }
+};
+
+// A ragged BN-row tile: rows at or past nvalid read row nvalid - 1 (nvalid >= 1).
+template <int NW, int BN, bool VTILE>
+__device__ __forceinline__ void stage_tile_n(GQA_LDS uint8_t* tile, const uint16_t* rows, size_t row_stride,
+                                             int nvalid, int wave, int lane) {
+#pragma unroll
+  for (int i = wave; i < BN / 4; i += NW) {
+    const int r = 4 * i + (lane >> 4);
+    const int slot = lane & 15;
+    const int c = slot ^ (VTILE ? swz_v(r) : swz_k(r));
+    const int gr = r < nvalid ? r : nvalid - 1;
+    lds_dma16(rows + (size_t)gr * row_stride + c * 8, tile + i * 1024);
+  }
+}
+
+// One BN-key tile for the NQ units of a wave (query rows q0[u] .. q0[u] + 31 of their
+// heads, Q fragments qreg[u]).
+template <bool CAUSAL, bool POS, int NB, int NQ>
+__device__ __forceinline__ void attend_tile_n(const GQA_LDS uint8_t* kt, const GQA_LDS uint8_t* vt, int t,
+                                              const int (&q0)[NQ], int S, float c, int lane,
+                                              const bf16x8 (&qreg)[NQ][8], RowState (&st)[NQ]) {
+  constexpr int BN = 32 * NB;
+  const int h = lane >> 5;
+  const int qi = lane & 31;
+  __builtin_amdgcn_s_setprio(1);
+  f32x16 s[NQ][NB];
+#pragma unroll
+  for (int u = 0; u < NQ; ++u)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) s[u][nb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bf16x8 kf = lds_read_k(kt, 32 * nb + qi, 2 * ks + h);
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) s[u][nb] = mfma32(kf, qreg[u][ks], s[u][nb]);
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+  const int key0 = t * BN;
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    if (!POS) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[u][nb][v] *= c;
+    }
+    const bool need_mask = CAUSAL ? (key0 + BN - 1 > q0[u]) : (key0 + BN > S);
+    if (need_mask) {
+      const int lim = CAUSAL ? (q0[u] + qi) : (S - 1);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (key0 + 32 * nb + 8 * (v >> 2) + 4 * h + (v & 3) > lim) s[u][nb][v] = -INFINITY;
+    }
+    float mx = s[u][0][0];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[u][nb][v]);
+    mx = halves_max(mx);
+    const float m_cand = fmaxf(st[u].m, POS ? mx * c : mx);
+    const bool upd = m_cand > st[u].m + kTau;
+    if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+      const float m_new = upd ? m_cand : st[u].m;
+      const float alpha = (m_new == st[u].m) ? 1.f : exp2_fast(st[u].m - m_new);
+      st[u].l *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) st[u].o[mb] *= alpha;
+      st[u].m = m_new;
+    }
+  }
+  const int g16 = lane >> 4;
+  const int li = lane & 15;
+  const int vrow = 4 * (g16 >> 1) + (li >> 2);
+  const int vcol = 16 * (g16 & 1) + 4 * (li & 3);
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int t4 = 0; t4 < 2 * NB; ++t4) {
+    s16x4 vlo[4], vhi[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      vlo[mb] = lds_read_v_tr(vt, 16 * t4 + vrow, 32 * mb + vcol);
+      vhi[mb] = lds_read_v_tr(vt, 16 * t4 + 8 + vrow, 32 * mb + vcol);
+    }
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const f32x16& sb = s[u][t4 >> 1];
+      const int o = 8 * (t4 & 1);
+      const float neg_m = -st[u].m;
+      float e[8];
+#pragma unroll
+      for (int w = 0; w < 8; ++w)
+        e[w] = exp2_fast(POS ? __builtin_fmaf(sb[o + w], c, neg_m) : sb[o + w] + neg_m);
+      const bf16x8 p = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      st[u].l = sum_bf16x8(p, st[u].l);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) st[u].o[mb] = mfma32(join_bf16x8(vlo[mb], vhi[mb]), p, st[u].o[mb]);
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// The prefill with BN-key tiles and NQ units (32 rows each) per wave, NW waves per
+// workgroup, all units of one KV head (workgroup ids as in prefill_kernel, longest first).
+// Each barrier publishes max(1, KB / BN) tiles, KB = 64 * (NW / 4) * NQ keys, through a
+// ring of twice that many stages (64 KB of LDS for NW = 4, NQ = 1, BN <= 64; 128 KB else).
+template <bool CAUSAL, bool POS, int NW, int NB, int NQ>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NQ == 1 && NW == 8 ? 2 : 1, 2)))
+void prefill_tiles_kernel(PrefillArgs a) {
+  constexpr int BN = 32 * NB;
+  constexpr int KB = 64 * (NW / 4) * NQ;
+  constexpr int P = KB / BN >= 1 ? KB / BN : 1;
+  constexpr int NST = 2 * P;
+  constexpr int kStage = BN * kRowBytes;   // bytes of one K (or V) tile
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv[NST][2][kStage];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;
+  const int qi = lane & 31;
+  const int bid = blockIdx.x;
+  const int slot = bid % a.nslots;
+  const int j = bid / a.nslots;
+  const int wg = CAUSAL ? (a.wgs_per_slot - 1 - j) : j;
+  const int b = slot / a.Hkv;
+  const int g = slot % a.Hkv;
+  const int nunits = a.G * a.nrb;
+  int unit[NQ], q0[NQ], head[NQ];
+  bool live[NQ];
+  int own_nt = 0;
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    unit[u] = NQ * (NW * wg + wave) + u;
+    live[u] = unit[u] < nunits;
+    const int rb = live[u] ? unit[u] / a.G : 0;
+    head[u] = g * a.G + (live[u] ? unit[u] % a.G : 0);
+    q0[u] = rb * 32;
+    if (live[u]) own_nt = max(own_nt, ((CAUSAL ? min(a.S, q0[u] + 32) : a.S) + BN - 1) / BN);
+  }
+  const int last_unit = min(NQ * NW * wg + NQ * NW - 1, nunits - 1);
+  const int kv_end = CAUSAL ? min(a.S, (last_unit / a.G) * 32 + 32) : a.S;
+  const int nt = (kv_end + BN - 1) / BN;
+
+  const size_t kv_stride = (size_t)a.Hkv * kD;
+  const uint16_t* kbase = a.k + ((size_t)b * a.S * a.Hkv + g) * kD;
+  const uint16_t* vbase = a.v + ((size_t)b * a.S * a.Hkv + g) * kD;
+  TileCopyN<NW, BN> copy;
+  copy.init(kv_stride, wave, lane);
+  auto kbuf = [&](int st) { return (GQA_LDS uint8_t*)lds_kv[st][0]; };
+  auto vbuf = [&](int st) { return (GQA_LDS uint8_t*)lds_kv[st][1]; };
+  auto issue_tile = [&](int t, int st) {
+    const int r0 = t * BN;
+    if (kv_end - r0 >= BN) {
+      copy.issue_full(kbuf(st), vbuf(st), kbase + (size_t)r0 * kv_stride, vbase + (size_t)r0 * kv_stride, wave);
+    } else {
+      stage_tile_n<NW, BN, false>(kbuf(st), kbase + (size_t)r0 * kv_stride, kv_stride, kv_end - r0, wave, lane);
+      stage_tile_n<NW, BN, true>(vbuf(st), vbase + (size_t)r0 * kv_stride, kv_stride, kv_end - r0, wave, lane);
+    }
+  };
+
+  issue_tile(0, 0);
+  bf16x8 qreg[NQ][8];
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    const int qrow = min(q0[u] + qi, a.S - 1);
+    const uint16_t* qp = a.q + (((size_t)b * a.S + qrow) * a.Hq + head[u]) * kD + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qreg[u][ks] = *(const bf16x8*)(qp + 16 * ks);
+  }
+  wait_vmcnt<0>();
+  for (int t = 1; t < P; ++t)
+    if (t < nt) issue_tile(t, t);
+
+  RowState st[NQ];
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    st[u].m = -INFINITY;
+    st[u].l = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) st[u].o[mb] = f32x16{};
+  }
+  for (int t = 0; t < nt; ++t) {
+    const int buf = t % NST;
+    if (buf % P == 0) {
+      // this wave's copies of tiles t .. t+P-1 land; after the barrier every wave's have,
+      // and every wave is done with the stages of tiles t-P .. t-1, which take t+P .. t+2P-1
+      wait_vmcnt<0>();
+      tile_barrier();
+      for (int i = 0; i < P; ++i)
+        if (t + P + i < nt) issue_tile(t + P + i, (buf + P + i) % NST);
+    }
+    if (t < own_nt) attend_tile_n<CAUSAL, POS, NB, NQ>(kbuf(buf), vbuf(buf), t, q0, a.S, a.c, lane, qreg, st);
+  }
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    const float l_tot = halves_sum(st[u].l);
+    const int qpos = q0[u] + qi;
+    if (live[u] && qpos < a.S) store_rows(a, b, qpos, head[u], h, l_tot, st[u]);
+  }
+}
+
+template <int NW, int NB, int NQ>
+static void launch_prefill_tiles_form(const PrefillArgs& a, bool causal, hipStream_t stream) {
+  const dim3 grid((unsigned)((size_t)a.nslots * a.wgs_per_slot));
+  const dim3 block(64 * NW);
+  const bool pos = a.c > 0.f;
+  if (causal) {
+    if (pos) hipLaunchKernelGGL((prefill_tiles_kernel<true, true, NW, NB, NQ>), grid, block, 0, stream, a);
+    else     hipLaunchKernelGGL((prefill_tiles_kernel<true, false, NW, NB, NQ>), grid, block, 0, stream, a);
+  } else {
+    if (pos) hipLaunchKernelGGL((prefill_tiles_kernel<false, true, NW, NB, NQ>), grid, block, 0, stream, a);
+    else     hipLaunchKernelGGL((prefill_tiles_kernel<false, false, NW, NB, NQ>), grid, block, 0, stream, a);
+  }
+}
+
+int launch_prefill_tiles(const PrefillArgs& a, bool causal, int rows_per_wave, int keys_per_tile, int waves,
+                         hipStream_t stream) {
+  const int key = 1000 * rows_per_wave + 10 * keys_per_tile + waves;
+  switch (key) {
+    case 32324: launch_prefill_tiles_form<4, 1, 1>(a, causal, stream); break;
+    case 32328: launch_prefill_tiles_form<8, 1, 1>(a, causal, stream); break;
+    case 33284: launch_prefill_tiles_form<4, 4, 1>(a, causal, stream); break;
+    case 33288: launch_prefill_tiles_form<8, 4, 1>(a, causal, stream); break;
+    case 64324: launch_prefill_tiles_form<4, 1, 2>(a, causal, stream); break;
+    case 64644: launch_prefill_tiles_form<4, 2, 2>(a, causal, stream); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
 int prefill_waves(int B, int S, int Hkv, int G) {
   // 8 waves once their grid holds at least 5/3 workgroups per CU (B = 1, 32 query and 8
   // KV heads: S > 3392). Paired timing on MI355X against the 4-wave form: x0.97 at 3072

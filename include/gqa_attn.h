@@ -107,6 +107,30 @@ int gqa_attn_prefill_form(const void* q, const void* k, const void* v, void* out
                           int waves, int key_splits, void* stream);
 
 /*
+ * The prefill with the tile shape fixed by the caller, for the sweep of tile shapes
+ * ("Field note 005", "The loop": the block and k-step sizes are the knobs a search
+ * turns; every point timed in paired rounds against the others). A unit is 32 query
+ * rows of one head; a wave owns rows_per_wave / 32 units, a workgroup `waves` waves,
+ * and K/V are staged through LDS in tiles of keys_per_tile keys. Supported
+ * (rows_per_wave, keys_per_tile, waves):
+ *   (32, 64, 4), (32, 64, 8)   the library's own 4- and 8-wave forms (as
+ *                              gqa_attn_prefill_form (4, 1) and (8, 1));
+ *   (32, 32, 4), (32, 32, 8)   32-key tiles;
+ *   (32, 128, 4), (32, 128, 8) 128-key tiles (the 4-wave one with 128 KB of LDS,
+ *                              one workgroup per CU);
+ *   (64, 32, 4), (64, 64, 4)   64 rows per wave: every K and V fragment read from LDS
+ *                              feeds two units' MFMAs; one wave per SIMD.
+ * Any other triple returns GQA_ATTN_ERR_UNSUPPORTED before any HIP call. Every shape
+ * computes the same attention (summation order and the lazy-rescale points differ, so
+ * results agree to bf16 rounding, not bit for bit). Same arguments, layout, errors and
+ * asynchrony as gqa_attn_prefill; with 128-key tiles Hkv must also stay below 132105
+ * (the 32-bit tile offsets). Allocates nothing.
+ */
+int gqa_attn_prefill_tiles(const void* q, const void* k, const void* v, void* out,
+                           int B, int S, int Hq, int Hkv, int D, float scale, int causal,
+                           int rows_per_wave, int keys_per_tile, int waves, void* stream);
+
+/*
  * One-token decode against a KV cache, split along the cache.
  *   q, out         : [B, Hq, D]  bf16
  *   kcache, vcache : [B, L, Hkv, D] bf16; L is the capacity (the row stride).

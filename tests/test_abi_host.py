@@ -254,3 +254,19 @@ def test_decode_noalloc_argument_errors(lib):
     assert call(L=1 << 21) == _lib.ERR_WORKSPACE
     assert b"scratch" in lib.gqa_attn_last_error()
     assert call(B=64, L=50000) == _lib.ERR_WORKSPACE
+
+
+def test_prefill_tiles_argument_errors(lib):
+    def tiles(bm, bn, nw, q=P, B=1, S=16, Hq=32, Hkv=8, D=128):
+        return lib.gqa_attn_prefill_tiles(q, P, P, P, B, S, Hq, Hkv, D, 0.088, 1, bm, bn, nw, None)
+    for bm, bn, nw in ((32, 16, 4), (32, 256, 4), (64, 128, 4), (64, 64, 8), (16, 64, 4), (32, 64, 2),
+                       (32, 32, 16), (0, 0, 0), (96, 64, 4)):
+        assert tiles(bm, bn, nw) == _lib.ERR_UNSUPPORTED, (bm, bn, nw)
+    assert tiles(32, 32, 4, q=None) == _lib.ERR_NULL
+    assert tiles(64, 64, 4, B=0) == _lib.ERR_DIM
+    assert tiles(32, 128, 8, D=64) == _lib.ERR_UNSUPPORTED
+    assert tiles(32, 32, 8, q=MIS) == _lib.ERR_UNSUPPORTED
+    # 128-key tiles address rows up to 127 with 32-bit offsets: Hkv <= 132104
+    assert 127 * 132104 * 256 + 255 < 2 ** 32 <= 127 * 132105 * 256 + 255
+    assert tiles(32, 128, 4, S=64, Hq=132105, Hkv=132105) == _lib.ERR_DIM
+    assert tiles(32, 128, 4, S=64, Hq=132105, Hkv=132105, q=MIS) == _lib.ERR_DIM

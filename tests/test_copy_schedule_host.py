@@ -3,9 +3,9 @@ two decode kernels, checked over a set of shapes (no GPU involved).
 
 The model restates, step by step, what the kernels' loops do with their copies: which K/V
 tile each wave copies at which step, into which LDS ring stage, from which global rows,
-and where each wave waits and meets a barrier (prefill.hip: prefill_kernel and
-prefill_split_kernel; decode.hip: decode_kernel; gqa_device.hpp: TileCopy and
-stage_tile). It checks, for every copy instruction and every lane:
+and where each wave waits and meets a barrier (prefill.hip: prefill_kernel,
+prefill_split_kernel, prefill_tiles_kernel with TileCopyN and stage_tile_n; decode.hip:
+decode_kernel; gqa_device.hpp: TileCopy and stage_tile). It checks, for every copy instruction and every lane:
 - the global bytes read lie inside the K or V tensor (row < S, or < lens[b] for a
   decode), and a full-tile copy's 32-bit byte offset does not wrap;
 - a full tile's 16 chunks x 64 rows are each fetched exactly once, into the LDS slot the
@@ -111,34 +111,51 @@ class Ring:
         self.readers[st].add(wave)
 
 
-def check_rows_in_bounds(t, kv_end, S, NW):
-    r0 = t * TILE
+def stage_tile_rows_n(nvalid, NW, wave, bn):
+    """stage_tile_n<NW, BN>: the global row each lane of each instruction of `wave` reads."""
+    rows = []
+    for i in range(wave, bn // 4, NW):
+        for lane in range(64):
+            r = 4 * i + (lane >> 4)
+            rows.append(r if r < nvalid else nvalid - 1)
+    return rows
+
+
+def check_rows_in_bounds(t, kv_end, S, NW, bn=TILE):
+    r0 = t * bn
     assert 0 <= t and r0 < kv_end <= S
-    if kv_end - r0 >= TILE:
-        assert r0 + TILE <= S                      # full tile: rows r0 .. r0+63
+    if kv_end - r0 >= bn:
+        assert r0 + bn <= S                        # full tile: rows r0 .. r0+bn-1
     else:
         for w in range(NW):
-            for r in stage_tile_rows(kv_end - r0, NW, w):
+            for r in stage_tile_rows_n(kv_end - r0, NW, w, bn):
                 assert 0 <= r0 + r < kv_end        # ragged tile: clamped to the last valid row
 
 
-def prefill_workgroup(NW, S, G, wg, causal=True):
-    """prefill_kernel<causal, *, NW>: the tiles one workgroup copies and reads, in order."""
-    P, NST = NW // 4, 2 * (NW // 4)
+def prefill_workgroup(NW, S, G, wg, causal=True, bn=TILE, nq=1):
+    """prefill_kernel<causal, *, NW> (bn = 64, nq = 1) or prefill_tiles_kernel<causal, *, NW,
+    bn / 32, nq>: the tiles one workgroup copies and reads, in order."""
+    P = max(1, 64 * (NW // 4) * nq // bn)
+    NST = 2 * P
     nrb = -(-S // 32)
     nunits = G * nrb
-    last_unit = min(NW * wg + NW - 1, nunits - 1)
+    per_wg = NW * nq
+    last_unit = min(per_wg * wg + per_wg - 1, nunits - 1)
     kv_end = min(S, (last_unit // G) * 32 + 32) if causal else S
-    nt = -(-kv_end // TILE)
+    nt = -(-kv_end // bn)
     ring = Ring(NST)
     own_nt = {}
     for w in range(NW):
-        unit = NW * wg + w
-        q0 = (unit // G) * 32 if unit < nunits else 0
-        own_nt[w] = -(-(min(S, q0 + 32) if causal else S) // TILE) if unit < nunits else 0
+        own_nt[w] = 0
+        for u in range(nq):
+            unit = nq * (NW * wg + w) + u
+            if unit < nunits:
+                q0 = (unit // G) * 32
+                own_nt[w] = max(own_nt[w], -(-(min(S, q0 + 32) if causal else S) // bn))
+    assert max(own_nt.values()) <= nt
 
     def issue(t, st):
-        check_rows_in_bounds(t, kv_end, S, NW)
+        check_rows_in_bounds(t, kv_end, S, NW, bn)
         ring.issue(st, t)
 
     issue(0, 0)
@@ -204,6 +221,33 @@ def test_prefill_copy_schedule(NW, S, G, causal):
     units = G * -(-S // 32)
     for wg in range(-(-units // NW)):
         prefill_workgroup(NW, S, G, wg, causal)
+
+
+@pytest.mark.parametrize("bm,bn,NW", [(32, 32, 4), (32, 32, 8), (32, 128, 4), (32, 128, 8), (64, 32, 4),
+                                      (64, 64, 4)])
+@pytest.mark.parametrize("S,G", PREFILL_SHAPES)
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_tile_shape_copy_schedule(bm, bn, NW, S, G, causal):
+    nq = bm // 32
+    units = G * -(-S // 32)
+    for wg in range(-(-units // (NW * nq))):
+        prefill_workgroup(NW, S, G, wg, causal, bn=bn, nq=nq)
+
+
+@pytest.mark.parametrize("NW,bn", [(4, 32), (8, 32), (4, 128), (8, 128)])
+def test_tile_copy_n_is_a_bijection(NW, bn):
+    seen = {"K": set(), "V": set()}
+    for wave in range(NW):
+        for j in range((bn // 4) // NW):
+            for lane in range(64):
+                r = 4 * (wave + NW * j) + (lane >> 4)
+                slot = lane & 15
+                for kind, swz in (("K", swz_k(r)), ("V", swz_v(r))):
+                    c = slot ^ swz
+                    assert (wave + NW * j) * 1024 + 16 * lane == r * ROW_BYTES + ((c ^ swz) << 4)
+                    assert (r, c) not in seen[kind]
+                    seen[kind].add((r, c))
+    assert len(seen["K"]) == len(seen["V"]) == bn * 16
 
 
 @pytest.mark.parametrize("S,G", PREFILL_SHAPES)
