@@ -771,6 +771,58 @@ def kernel_sizes(path: str, timed: int = 200):
             f.write(json.dumps(r) + "\n")
 
 
+READ_FLOOR_L = (16384, 32768, 65536)
+READ_FLOOR_WORKGROUPS = (256, 512, 1024)
+
+
+def read_floor(path: str, timed: int = 100, settle: int = 200):
+    """The cold pure-read floor under a decode: the library's HBM read probe over exactly
+    the bytes of a batch-1 decode's K and V (4096 * L) for each L of READ_FLOOR_L, with 256
+    workgroups (one per CU, the decode's grid at batch 1), 512 and 1024, each buffer one of
+    >= 1 GB of copies in rotation so no call finds it in the MALL. Per point `settle` calls,
+    then `timed` calls between HIP events; one JSON line per point with its call counts, for
+    kernel_stats.py --read-floor to match against a rocprofv3 kernel trace:
+        rocprofv3 --kernel-trace --output-format csv -d DIR -o floor -- python3 bench.py --read-floor OUT
+    Nothing but the read happens: no arithmetic, no merge. A decode of the same cache can
+    not take less kernel time than the best of these points."""
+    import statistics
+    import torch
+    from gqa_flash_attention_amd import _lib
+    lib = _lib.get()
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    rows = []
+    for L in READ_FLOOR_L:
+        nbytes = L * HKV * D * 2 * 2
+        nc = max(4, (1 << 30) // nbytes)
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(nc)]
+        for wg in READ_FLOOR_WORKGROUPS:
+            sink = torch.empty(wg * 256, dtype=torch.int32, device=dev)
+
+            def call(i):
+                _lib.check(lib.gqa_attn_probe_hbm_read(bufs[i % nc].data_ptr(), nbytes, wg, sink.data_ptr(),
+                                                       sink.numel(), st.cuda_stream), "gqa_attn_probe_hbm_read")
+            for i in range(settle):
+                call(i)
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(timed)]
+            for i in range(timed):
+                ev[i][0].record(st)
+                call(settle + i)
+                ev[i][1].record(st)
+            torch.cuda.synchronize()
+            ms = statistics.median(a.elapsed_time(b) for a, b in ev)
+            r = {"mode": "read_floor", "L": L, "bytes": nbytes, "workgroups": wg, "settle_calls": settle,
+                 "timed_calls": timed, "event_us_median": round(ms * 1e3, 2)}
+            print(json.dumps(r), flush=True)
+            rows.append(r)
+        del bufs
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        for r in rows:
+            f.write(json.dumps(r) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -789,6 +841,8 @@ def main():
                     help="prefill workgroup-form sweep with paired timing (see sweep_forms)")
     ap.add_argument("--sweep-tiles", metavar="OUT_JSONL", default=None,
                     help="prefill tile-shape sweep with paired timing (see sweep_tiles)")
+    ap.add_argument("--read-floor", metavar="OUT_JSONL", default=None,
+                    help="cold pure-read floor at the decode sizes, for a kernel trace (see read_floor)")
     ap.add_argument("--kernel-sizes", metavar="OUT_JSONL", default=None,
                     help="every prefill/decode size back to back, for a rocprofv3 kernel trace (see kernel_sizes)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -810,6 +864,8 @@ def main():
         sweep_forms(args.sweep_forms)
     elif args.sweep_tiles:
         sweep_tiles(args.sweep_tiles)
+    elif args.read_floor:
+        read_floor(args.read_floor)
     elif args.kernel_sizes:
         kernel_sizes(args.kernel_sizes)
     else:

@@ -192,16 +192,72 @@ def summarize_sizes(prof_dir: str, sizes_jsonl: str, out_md: str, out_json: str)
     return text
 
 
+FLOOR_CMD = ("rocprofv3 --kernel-trace --output-format csv -d <dir> -o floor -- "
+             "python3 bench.py --read-floor floor.jsonl")
+
+
+def summarize_read_floor(prof_dir: str, floor_jsonl: str, out_md: str, decode_json: str | None) -> str:
+    """Kernel time of each read-floor point (bench.py --read-floor), matched in dispatch order,
+    beside the decode's own kernel time at the same L (profiles/kernel_time.json) when given."""
+    paths = glob.glob(os.path.join(prof_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_trace.csv under {prof_dir}")
+    disp = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                  for r in csv.DictReader(open(paths[0])) if "probe_hbm_read" in r["Kernel_Name"])
+    rows = [json.loads(ln) for ln in open(floor_jsonl) if ln.strip()]
+    dec = {}
+    if decode_json and os.path.exists(decode_json):
+        dec = json.load(open(decode_json)).get("sizes", {})
+    pos = 0
+    lines = ["# Cold pure-read floor at the decode sizes (batch 1, K + V of 8 KV heads x 128 bf16)", "",
+             "Commands (repository root, library built in-tree beforehand):", "", "```", "export TMPDIR=/tmp",
+             FLOOR_CMD, "python -m gqa_flash_attention_amd.kernel_stats --read-floor <dir> floor.jsonl", "```", "",
+             "The library's HBM read probe (`gqa_attn_probe_hbm_read`: 16-byte non-temporal loads, the workgroups "
+             "of each XCD reading one 256-byte slice of every 2 KB row, as the decode does) reads exactly the "
+             "bytes of a batch-1 decode's K and V cache (4096 L), from one of >= 1 GB of buffers in rotation so "
+             "the MALL holds none. It does no arithmetic and no merge: a decode of the same cache cannot finish "
+             "in less kernel time than the best point. Decode kernel times are from "
+             "`profiles/kernel_time.json` (same kernel-trace method, a run on another box).", "",
+             "| L | bytes | workgroups | read kernel us (median) | GB/s | fraction of 8 TB/s | decode kernel us | "
+             "decode / best read |", "|---|---|---|---|---|---|---|---|"]
+    best = {}
+    table = []
+    for r in rows:
+        n0, n1 = r["settle_calls"], r["timed_calls"]
+        seq = disp[pos: pos + n0 + n1]
+        if len(seq) != n0 + n1:
+            raise SystemExit(f"trace holds {len(seq)} probe dispatches for {r}, expected {n0 + n1}")
+        pos += n0 + n1
+        med = statistics.median(d for _, d in seq[n0:]) / 1e3
+        best[r["L"]] = min(best.get(r["L"], 1e30), med)
+        table.append((r, med))
+    for r, med in table:
+        d = dec.get(f"decode_L{r['L']}")
+        dk = f"{d['kernel_us_median']:.2f}" if d else "-"
+        ratio = f"{d['kernel_us_median'] / best[r['L']]:.2f}" if d else "-"
+        lines.append(f"| {r['L']} | {r['bytes']} | {r['workgroups']} | {med:.2f} | {r['bytes'] / med / 1e3:.0f} | "
+                     f"{r['bytes'] / med / 1e3 / 8000:.3f} | {dk} | {ratio} |")
+    text = "\n".join(lines) + "\n"
+    with open(out_md, "w") as f:
+        f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("prof_dir")
     ap.add_argument("bench_json", help="the bench's JSON line, or with --sizes the --kernel-sizes JSONL")
     ap.add_argument("--sizes", action="store_true",
                     help="summarize a trace of `bench.py --kernel-sizes` into per-size kernel times")
+    ap.add_argument("--read-floor", action="store_true",
+                    help="summarize a trace of `bench.py --read-floor` (the cold pure-read floor)")
     ap.add_argument("--out", default=None)
     ap.add_argument("--out-json", default=os.path.join(ROOT, "profiles", "kernel_time.json"))
     a = ap.parse_args()
-    if a.sizes:
+    if a.read_floor:
+        out = a.out or os.path.join(ROOT, "profiles", "hbm_read_floor_decode_sizes.md")
+        print(summarize_read_floor(a.prof_dir, a.bench_json, out, os.path.join(ROOT, "profiles", "kernel_time.json")))
+    elif a.sizes:
         out = a.out or os.path.join(ROOT, "profiles", "kernel_time_prefill_decode_sizes.md")
         print(summarize_sizes(a.prof_dir, a.bench_json, out, a.out_json))
     else:

@@ -131,3 +131,77 @@ def test_kernel_stats_summary_rates(tmp_path):
     assert f"decode {bench.decode_bytes(L) / 5.0e4:.0f} GB/s" in text
     assert f"MFMA probe {bench.probe_mfma_flops() / 1.45e7 / 1e3:.0f} TFLOP/s" in text
     assert (tmp_path / "out.md").read_text() == text
+
+
+TRACE_FIELDS = ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+
+
+def _trace(d, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "x_kernel_trace.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=TRACE_FIELDS)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_kernel_sizes_match_dispatches_in_order(tmp_path):
+    from gqa_flash_attention_amd import kernel_stats
+    # two prefill sizes and one decode size; a workspace fill kernel in between is ignored
+    sizes = [{"mode": "prefill", "S": 4096, "settle_calls": 2, "timed_calls": 3, "event_ms_median": 0.2,
+              "event_ms_p05": 0.19, "event_ms_p95": 0.21, "event_ms_min": 0.18, "flops": bench.prefill_flops(4096)},
+             {"mode": "prefill", "S": 8192, "settle_calls": 1, "timed_calls": 3, "event_ms_median": 0.6,
+              "event_ms_p05": 0.55, "event_ms_p95": 0.65, "event_ms_min": 0.5, "flops": bench.prefill_flops(8192)},
+             {"mode": "decode", "L": 16384, "settle_calls": 1, "timed_calls": 2, "event_ms_median": 0.02,
+              "event_ms_p05": 0.02, "event_ms_p95": 0.02, "event_ms_min": 0.02, "bytes": bench.decode_bytes(16384)}]
+    t, rows = 0, []
+
+    def k(name, ns):
+        nonlocal t
+        rows.append({"Kind": "KERNEL_DISPATCH", "Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + ns})
+        t += ns + 1000
+    for ns in (999, 999, 100000, 110000, 120000):            # S = 4096: 2 settling, median 110 us
+        k(PREFILL, ns)
+    for ns in (1, 400000, 500000, 450000):                   # S = 8192: median 450 us
+        k(PREFILL, ns)
+    k("gqa::fill_words_kernel(unsigned int*, unsigned long, unsigned int)", 5)
+    for ns in (7, 16000, 18000):                             # L = 16384: median 17 us
+        k(DECODE, ns)
+    _trace(tmp_path / "tr", rows)
+    with open(tmp_path / "sizes.jsonl", "w") as f:
+        for r in sizes:
+            f.write(json.dumps(r) + "\n")
+    kernel_stats.summarize_sizes(str(tmp_path / "tr"), str(tmp_path / "sizes.jsonl"), str(tmp_path / "o.md"),
+                                 str(tmp_path / "o.json"))
+    res = json.load(open(tmp_path / "o.json"))["sizes"]
+    assert res["prefill_S4096"]["kernel_us_median"] == pytest.approx(110.0)
+    assert res["prefill_S8192"]["kernel_us_median"] == pytest.approx(450.0)
+    assert res["decode_L16384"]["kernel_us_median"] == pytest.approx(17.0)
+    assert res["decode_L16384"]["frac_kernel"] == pytest.approx(bench.decode_bytes(16384) / 17e-6 / 8e12)
+    assert res["prefill_S8192"]["tflops_kernel"] == pytest.approx(bench.prefill_flops(8192) / 450e-6 / 1e12)
+    # a dispatch count that does not add up is an error, not a silent mismatch
+    rows.append({"Kind": "KERNEL_DISPATCH", "Kernel_Name": DECODE, "Start_Timestamp": t, "End_Timestamp": t + 1})
+    _trace(tmp_path / "tr2", rows)
+    with pytest.raises(SystemExit):
+        kernel_stats.summarize_sizes(str(tmp_path / "tr2"), str(tmp_path / "sizes.jsonl"), str(tmp_path / "o.md"),
+                                     str(tmp_path / "o.json"))
+
+
+def test_read_floor_points_match_probe_dispatches(tmp_path):
+    from gqa_flash_attention_amd import kernel_stats
+    probe = "gqa::(anonymous namespace)::probe_hbm_read_kernel(unsigned int __vector(4) const*, unsigned long, unsigned int*, int)"
+    pts = [{"mode": "read_floor", "L": 16384, "bytes": 16384 * 4096, "workgroups": wg, "settle_calls": 1,
+            "timed_calls": 3, "event_us_median": 15.0} for wg in (256, 512)]
+    t, rows = 0, []
+    for durs in ((1, 12000, 12500, 13000), (1, 10800, 11000, 10900)):
+        for ns in durs:
+            rows.append({"Kind": "KERNEL_DISPATCH", "Kernel_Name": probe, "Start_Timestamp": t, "End_Timestamp": t + ns})
+            t += ns + 100
+    _trace(tmp_path / "tr", rows)
+    with open(tmp_path / "f.jsonl", "w") as f:
+        for r in pts:
+            f.write(json.dumps(r) + "\n")
+    text = kernel_stats.summarize_read_floor(str(tmp_path / "tr"), str(tmp_path / "f.jsonl"), str(tmp_path / "o.md"),
+                                             None)
+    assert "| 16384 | 67108864 | 256 | 12.50 |" in text
+    assert "| 16384 | 67108864 | 512 | 10.90 |" in text
