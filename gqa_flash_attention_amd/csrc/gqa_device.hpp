@@ -165,10 +165,15 @@ __device__ __forceinline__ void halves(float x, float& lo, float& hi) {
   lo = __uint_as_float(r[0]);
   hi = __uint_as_float(r[1]);
 }
+// IEEE 754-2019 maximum (v_maximum3_f32 on gfx950): unlike fmaxf it needs no quieting of
+// its operands first, which the compiler otherwise emits as extra v_max_f32 x, x, x. NaN
+// operands propagate; -inf (masked scores, an empty running max) behaves as in fmaxf.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float halves_max(float x) {
   float a, b;
   halves(x, a, b);
-  return fmaxf(a, b);
+  return vmax(a, b);
 }
 __device__ __forceinline__ float halves_sum(float x) {
   float a, b;

@@ -111,11 +111,11 @@ __device__ __forceinline__ void attend_tile(const GQA_LDS uint8_t* kt, const GQA
   }
   float mx = s0[0];
 #pragma unroll
-  for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s0[v]);
+  for (int v = 1; v < 16; ++v) mx = vmax(mx, s0[v]);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s1[v]);
+  for (int v = 0; v < 16; ++v) mx = vmax(mx, s1[v]);
   mx = halves_max(mx);
-  const float m_cand = fmaxf(st.m, POS ? mx * c : mx);
+  const float m_cand = vmax(st.m, POS ? mx * c : mx);
   const bool upd = m_cand > st.m + kTau;
   if (__builtin_amdgcn_ballot_w64(upd) != 0) {
     const float m_new = upd ? m_cand : st.m;
@@ -543,9 +543,9 @@ __device__ __forceinline__ void attend_tile_n(const GQA_LDS uint8_t* kt, const G
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[u][nb][v]);
+      for (int v = 0; v < 16; ++v) mx = vmax(mx, s[u][nb][v]);
     mx = halves_max(mx);
-    const float m_cand = fmaxf(st[u].m, POS ? mx * c : mx);
+    const float m_cand = vmax(st[u].m, POS ? mx * c : mx);
     const bool upd = m_cand > st[u].m + kTau;
     if (__builtin_amdgcn_ballot_w64(upd) != 0) {
       const float m_new = upd ? m_cand : st[u].m;

@@ -61,6 +61,16 @@ def test_full_tile_copy_is_a_bijection_onto_the_swizzled_layout(NW):
     assert len(seen["K"]) == len(seen["V"]) == TILE * 16
 
 
+@pytest.mark.parametrize("NW", [4, 8])
+def test_every_wave_issues_the_same_number_of_copies_per_tile_full_or_ragged(NW):
+    # the decode waits with vmcnt = (tiles still allowed in flight) x (copies per wave per
+    # tile), so a ragged tile must cost each wave as many copy instructions as a full one
+    full = 2 * ((TILE // 4) // NW)                              # TileCopy<NW>: K and V
+    for wave in range(NW):
+        ragged = 2 * len(range(wave, TILE // 4, NW))            # stage_tile<NW>: K and V
+        assert ragged == full
+
+
 @pytest.mark.parametrize("Hkv", [1, 8, 1000, 266305])
 def test_full_tile_offsets_fit_32_bits_for_every_accepted_head_count(Hkv):
     # the library accepts Hkv <= 266305 (plan_prefill); the largest offset then fits
@@ -258,8 +268,14 @@ def test_prefill_split_copy_schedule(S, G, causal):
         prefill_split_workgroup(S, G, wg, causal)
 
 
+DEC_WAVES = 4        # decode waves that attend (16 keys of each tile each)
+DEC_COPY_WAVES = 8   # decode waves that issue the tile copies
+
+
 def decode_workgroup(L, length, nsplit, chunk, split, strided, nstage=4):
-    """decode_kernel<nstage, fused, strided> for one split: the keys of each tile it streams."""
+    """decode_kernel<nstage, fused, strided> for one split: the keys of each tile it streams.
+    All DEC_COPY_WAVES waves issue copies and meet every tile barrier; the first DEC_WAVES
+    read the tiles."""
     T = -(-length // TILE)
     if strided:
         ntiles = (T - 1 - split) // nsplit + 1 if split < T else 0
@@ -278,8 +294,8 @@ def decode_workgroup(L, length, nsplit, chunk, split, strided, nstage=4):
         if length - r0 >= TILE:
             assert r0 + TILE <= length
         else:
-            for w in range(4):
-                for r in stage_tile_rows(length - r0, 4, w):
+            for w in range(DEC_COPY_WAVES):
+                for r in stage_tile_rows(length - r0, DEC_COPY_WAVES, w):
                     assert 0 <= r0 + r < length
         ring.issue(t % nstage, t)
 
@@ -299,7 +315,7 @@ def decode_workgroup(L, length, nsplit, chunk, split, strided, nstage=4):
             issue(t + nstage - 1)
             issued += 1
         ks = key(t)
-        for w in range(4):
+        for w in range(DEC_WAVES):
             if ks + 16 * w < length:
                 ring.read(t % nstage, t, w)
         keys.extend(range(ks, min(ks + TILE, length)))
