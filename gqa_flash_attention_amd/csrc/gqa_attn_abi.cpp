@@ -141,11 +141,11 @@ int get_workspace(size_t need, hipStream_t stream, void** out) {
 constexpr size_t kScratchBytes = size_t(8) << 20;
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
-struct ScratchState {
-  void* ptr = nullptr;   // the device address of `scratch` on that device
-};
+// The device address of `scratch` per device ordinal, looked up once; a fixed table, so that
+// the entry point allocates no host memory either.
+constexpr int kMaxScratchDevices = 64;
 std::mutex g_scratch_mutex;
-std::map<int, ScratchState> g_scratch;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
 
 // With g_scratch_mutex held: the address of the current device's scratch. The first call on
 // a device looks the address up and clears the whole array (a kernel on `stream`, so the
@@ -154,16 +154,16 @@ int scratch_on_current_device(hipStream_t stream, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail("hipGetDevice", e);
-  ScratchState& st = g_scratch[dev];
-  if (!st.ptr) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return hip_fail("scratch: device ordinal out of range", hipErrorInvalidDevice);
+  if (!g_scratch_ptr[dev]) {
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (e != hipSuccess || !p) return hip_fail("hipGetSymbolAddress(scratch)", e != hipSuccess ? e : hipErrorUnknown);
     const int fe = gqa::launch_fill_words((uint32_t*)p, kScratchBytes / 4, 0u, stream);
     if (fe != 0) return hip_fail("fill_words launch (scratch)", fe);
-    st.ptr = p;
+    g_scratch_ptr[dev] = p;
   }
-  *out = st.ptr;
+  *out = g_scratch_ptr[dev];
   return 0;
 }
 

@@ -217,7 +217,8 @@ int gqa_attn_decode_ws(const void* q, const void* kcache, const void* vcache,
  * L = 2^20). The first call on a GPU also clears that GPU's scratch with a
  * small kernel on `stream`. Every call on one GPU shares its scratch: calls
  * that overlap in time on one GPU (other streams, other threads) race and must
- * be serialised by the caller.
+ * be serialised by the caller. Device ordinals 0-63 are supported (others
+ * return GQA_ATTN_ERR_HIP).
  */
 int gqa_attn_decode_noalloc(const void* q, const void* kcache, const void* vcache,
                             const int32_t* lens, void* out,
