@@ -458,15 +458,16 @@ int decode_default_chunk(int B, int L, int Hkv, int G) {
   // on MI355X with the fused decode's strided splits: batch 1, L = 2K..64K: 128-key splits
   // are fastest at 2K, ~L/32 from 16K up; batched caches (B = 4..64, uniform or ragged
   // lengths up to 50001) run as fast or faster with 4096-key splits than with 1024 (up to
-  // 11% at B = 64, L = 4K, and 10% for a ragged batch of 16). Splits of fewer than 4 tiles
-  // are raised to 4 while that still leaves at least 128 workgroups: at batch 1 and 4K keys,
-  // 256-key splits (128 workgroups) are 8% faster than 128-key ones (256 workgroups),
-  // while at 2K (64 workgroups) they are 4% slower.
+  // 11% at B = 64, L = 4K, and 10% for a ragged batch of 16). Splits of fewer than 8 tiles
+  // are doubled while that still leaves at least 128 workgroups: at batch 1, 256-key splits
+  // (128 workgroups) are 8% faster than 128-key ones (256 workgroups) at 4K keys and
+  // 512-key ones 2% faster than 256 at 8K, while at 2K 256-key splits (64 workgroups) are
+  // 3% slower than 128.
   const long long slots = (long long)B * Hkv * ((G + 15) / 16);
   const long long per = ((long long)L * slots + 255) / 256;
   long long chunk = (per + kTileRows - 1) / kTileRows * kTileRows;
   if (chunk < 2 * kTileRows) chunk = 2 * kTileRows;
-  if (chunk < 4 * kTileRows && ((long long)L / (4 * kTileRows)) * slots >= 128) chunk = 4 * kTileRows;
+  while (chunk < 8 * kTileRows && ((long long)L / (2 * chunk)) * slots >= 128) chunk *= 2;
   if (chunk > 4096) chunk = 4096;
   return (int)chunk;
 }

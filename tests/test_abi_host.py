@@ -170,8 +170,8 @@ def test_decode_plan_and_workspace_size(lib):
         counters = max(4096, 32)
         assert ws == ((counters * 4 + 255) // 256 * 256 + (rows * 128 * 4 + 255) // 256 * 256
                       + (rows * 4 + 255) // 256 * 256)
-    # short caches: splits of at least 4 tiles once that leaves >= 128 workgroups
-    for L, want in ((2048, 128), (3000, 128), (4096, 256), (8192, 256)):
+    # short caches: splits doubled up to 8 tiles while that leaves >= 128 workgroups
+    for L, want in ((2048, 128), (3000, 128), (4096, 256), (6000, 192), (8192, 512), (12000, 384), (16384, 512)):
         assert lib.gqa_attn_decode_plan(1, L, 32, 8, 128, ctypes.byref(chunk), ctypes.byref(nsplit)) == 0
         assert chunk.value == want, (L, chunk.value)
     # batch-1 decodes of the workload are cut into about one chunk per CU (256 CUs)
