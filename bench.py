@@ -711,6 +711,8 @@ def sweep(path, steps, warmup):
 
 KERNEL_SIZES_PREFILL = (2048, 4096, 8192, 16384, 32768)
 KERNEL_SIZES_DECODE = (2048, 4096, 8192, 16384, 32768, 65536)
+# batched decodes, every sequence at the full cache length, as in --sweep
+KERNEL_SIZES_DECODE_BATCHED = ((32, 16384), (16, 32768), (8, 65536), (64, 4096))
 
 
 def kernel_sizes(path: str, timed: int = 200):
@@ -766,6 +768,30 @@ def kernel_sizes(path: str, timed: int = 200):
             {"bytes": decode_bytes(L), "copies_rotated": nc})
         del kcs, vcs
         torch.cuda.empty_cache()
+    from gqa_inputs import randn_bf16_device
+    for B, L in KERNEL_SIZES_DECODE_BATCHED:
+        qd = randn_bf16_device((B, HQ, D), seed_base(4, 4), dev)
+        kcs = [randn_bf16_device((B, L, HKV, D), seed_base(4, 4) + 10 + i, dev) for i in range(2)]
+        vcs = [randn_bf16_device((B, L, HKV, D), seed_base(4, 4) + 30 + i, dev) for i in range(2)]
+        lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+        out = torch.empty_like(qd)
+        run("decode", L, lambda i: gqa.decode(qd, kcs[i % 2], vcs[i % 2], lens, out=out), 0.3,
+            {"B": B, "bytes": decode_bytes(B * L, B), "copies_rotated": 2})
+        del kcs, vcs
+        torch.cuda.empty_cache()
+    # the ragged batch of --sweep and the parity tests: B = 16, lengths U[1, 50001]
+    B, L = 16, 50001
+    from gqa_inputs import random_lens
+    lens_h = random_lens(B, 1, L, seed=seed_base(4, 3) + 3)
+    qd = randn_bf16_device((B, HQ, D), seed_base(4, 3), dev)
+    kcs = [randn_bf16_device((B, L, HKV, D), seed_base(4, 3) + 10 + i, dev) for i in range(2)]
+    vcs = [randn_bf16_device((B, L, HKV, D), seed_base(4, 3) + 20 + i, dev) for i in range(2)]
+    lens = lens_h.to(dev)
+    out = torch.empty_like(qd)
+    run("decode", L, lambda i: gqa.decode(qd, kcs[i % 2], vcs[i % 2], lens, out=out), 0.3,
+        {"B": B, "ragged": True, "bytes": decode_bytes(int(lens_h.sum()), B), "copies_rotated": 2})
+    del kcs, vcs
+    torch.cuda.empty_cache()
     with open(path, "w") as f:
         for r in rows:
             f.write(json.dumps(r) + "\n")

@@ -159,7 +159,9 @@ def summarize_sizes(prof_dir: str, sizes_jsonl: str, out_md: str, out_json: str)
             e["frac_kernel"] = e["tflops_kernel"] / bench.PEAK_BF16_TFLOPS
             e["tflops_event"] = r["flops"] / (r["event_ms_median"] * 1e-3) / 1e12
         else:
-            key = f"decode_L{r['L']}"
+            # batch-1 decodes by length; batched and ragged ones also by batch
+            key = f"decode_L{r['L']}" if r.get("B", 1) == 1 else (
+                f"decode_B{r['B']}_L{r['L']}" + ("_ragged" if r.get("ragged") else ""))
             e["gbs_kernel"] = r["bytes"] / (med * 1e-9) / 1e9
             e["frac_kernel"] = e["gbs_kernel"] / bench.PEAK_HBM_GBS
             e["gbs_event"] = r["bytes"] / (r["event_ms_median"] * 1e-3) / 1e9
@@ -170,14 +172,17 @@ def summarize_sizes(prof_dir: str, sizes_jsonl: str, out_md: str, out_json: str)
     doc = {"sources_digest": bench.kernel_sources_digest(), "command": SIZES_CMD, "sizes": res}
     with open(out_json, "w") as f:
         json.dump(doc, f, indent=1)
-    lines = ["# Kernel time per workload size: causal prefill and decode, B = 1, 32 query / 8 KV heads, d = 128, bf16",
+    lines = ["# Kernel time per workload size: causal prefill and decode, B = 1 (and batched decodes), 32 query / 8 KV "
+             "heads, d = 128, bf16",
              "", "Commands (repository root, library built in-tree beforehand with "
              "`python -m gqa_flash_attention_amd.build`):", "", "```", "export TMPDIR=/tmp", SIZES_CMD,
              "python -m gqa_flash_attention_amd.kernel_stats --sizes <dir> sizes.jsonl", "```", "",
              f"Kernel sources digest `{doc['sources_digest']}`. Per size: ~0.2 s of settling calls, then the timed "
              "calls; kernel time is each dispatch's own duration in the trace, the event span is the bench's HIP "
              "events around each call (it also holds the dispatch). Decode caches rotate over >= 1 GB of copies, "
-             "so each decode reads from HBM. Fractions are of 2.5 PFLOP/s (bf16 dense) and 8 TB/s.", "",
+             "so each decode reads from HBM. decode_B<B>_L<L> rows are batched decodes with every sequence at the "
+             "full length; the _ragged row has lengths U[1, L] (bytes counted over the actual lengths). Fractions "
+             "are of 2.5 PFLOP/s (bf16 dense) and 8 TB/s.", "",
              "| size | kernel | calls | kernel us median (p05-p95) | event us median | rate by kernel time | "
              "fraction of peak |", "|---|---|---|---|---|---|---|"]
     for key, e in res.items():

@@ -153,7 +153,12 @@ def test_kernel_sizes_match_dispatches_in_order(tmp_path):
              {"mode": "prefill", "S": 8192, "settle_calls": 1, "timed_calls": 3, "event_ms_median": 0.6,
               "event_ms_p05": 0.55, "event_ms_p95": 0.65, "event_ms_min": 0.5, "flops": bench.prefill_flops(8192)},
              {"mode": "decode", "L": 16384, "settle_calls": 1, "timed_calls": 2, "event_ms_median": 0.02,
-              "event_ms_p05": 0.02, "event_ms_p95": 0.02, "event_ms_min": 0.02, "bytes": bench.decode_bytes(16384)}]
+              "event_ms_p05": 0.02, "event_ms_p95": 0.02, "event_ms_min": 0.02, "bytes": bench.decode_bytes(16384)},
+             {"mode": "decode", "L": 4096, "B": 64, "settle_calls": 1, "timed_calls": 2, "event_ms_median": 0.2,
+              "event_ms_p05": 0.2, "event_ms_p95": 0.2, "event_ms_min": 0.2, "bytes": bench.decode_bytes(64 * 4096)},
+             {"mode": "decode", "L": 50001, "B": 16, "ragged": True, "settle_calls": 1, "timed_calls": 2,
+              "event_ms_median": 0.3, "event_ms_p05": 0.3, "event_ms_p95": 0.3, "event_ms_min": 0.3,
+              "bytes": bench.decode_bytes(390221)}]
     t, rows = 0, []
 
     def k(name, ns):
@@ -167,6 +172,10 @@ def test_kernel_sizes_match_dispatches_in_order(tmp_path):
     k("gqa::fill_words_kernel(unsigned int*, unsigned long, unsigned int)", 5)
     for ns in (7, 16000, 18000):                             # L = 16384: median 17 us
         k(DECODE, ns)
+    for ns in (7, 150000, 160000):                           # B = 64, L = 4096: median 155 us
+        k(DECODE, ns)
+    for ns in (7, 240000, 260000):                           # ragged B = 16: median 250 us
+        k(DECODE, ns)
     _trace(tmp_path / "tr", rows)
     with open(tmp_path / "sizes.jsonl", "w") as f:
         for r in sizes:
@@ -178,6 +187,8 @@ def test_kernel_sizes_match_dispatches_in_order(tmp_path):
     assert res["prefill_S8192"]["kernel_us_median"] == pytest.approx(450.0)
     assert res["decode_L16384"]["kernel_us_median"] == pytest.approx(17.0)
     assert res["decode_L16384"]["frac_kernel"] == pytest.approx(bench.decode_bytes(16384) / 17e-6 / 8e12)
+    assert res["decode_B64_L4096"]["kernel_us_median"] == pytest.approx(155.0)
+    assert res["decode_B16_L50001_ragged"]["gbs_kernel"] == pytest.approx(bench.decode_bytes(390221) / 250e-6 / 1e9)
     assert res["prefill_S8192"]["tflops_kernel"] == pytest.approx(bench.prefill_flops(8192) / 450e-6 / 1e12)
     # a dispatch count that does not add up is an error, not a silent mismatch
     rows.append({"Kind": "KERNEL_DISPATCH", "Kernel_Name": DECODE, "Start_Timestamp": t, "End_Timestamp": t + 1})
